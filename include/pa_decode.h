@@ -1,0 +1,171 @@
+/*
+ * pa_decode.h -- paged decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpa_decode.so.  Every pointer argument named *_cache, query,
+ * block_tables, seq_lens, out or workspace is a DEVICE pointer owned by the
+ * caller; the library allocates nothing, keeps no device state between calls
+ * and never synchronises the stream.  All compute entry points are
+ * asynchronous on `stream` (a hipStream_t; NULL is the default stream).
+ *
+ * The operation (pages "Paged Attention > The PagedAttention Algorithm",
+ * sections "Standard Attention vs PagedAttention" and "Optimized CUDA
+ * Kernels"; "PagedAttention by hand", sections "Setup" and "Forward pass",
+ * Steps 2-4; glossary "PagedAttention", section "How It Works"): for every
+ * sequence s and query head h, with L = seq_lens[s] and kv head
+ * g = h / (Hq / Hkv),
+ *
+ *     token t (0 <= t < L) lives in physical block block_tables[s][t / B]
+ *     at slot t % B;
+ *     x_t  = scale * dot(query[s][h], K[t]);
+ *     p_t  = exp(x_t - max_u x_u) / sum_u exp(x_u - max_u x_u);
+ *     out[s][h] = sum_t p_t * V[t];
+ *
+ * and out[s][h] = 0 when L = 0.  Slots at or past L in a sequence's last
+ * block, and table entries at or past ceil(L / B), are never read: their
+ * contents (NaN included) cannot reach the output.
+ *
+ * Layouts (row-major, densely packed, element type `dtype`):
+ *     query        [S][Hq][D]
+ *     key_cache    [NB][Hkv][B][D]
+ *     value_cache  [NB][Hkv][B][D]
+ *     block_tables [S][max_blocks]   int32
+ *     seq_lens     [S]               int32
+ *     out          [S][Hq][D]        element type `out_dtype`
+ *
+ * Preconditions on device data (the caller guarantees them; they are not
+ * checked): 0 <= seq_lens[s] <= max_blocks * B, and
+ * 0 <= block_tables[s][j] < NB for every j < ceil(seq_lens[s] / B).
+ *
+ * Arithmetic: fp32 accumulation for fp16 / bf16 inputs; the output is rounded
+ * to `out_dtype` (round to nearest even) once, at the end.
+ */
+#ifndef PA_DECODE_H
+#define PA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Status codes.  Every entry point validates its host-side arguments before
+ * launching anything; on a non-OK status nothing was launched. */
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    PA_ERR_SHAPE = 2,       /* negative / zero size, Hq % Hkv != 0, size overflow */
+    PA_ERR_UNSUPPORTED = 3, /* dtype, head size or kernel choice not supported  */
+    PA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned       */
+    PA_ERR_HIP = 5          /* the HIP runtime reported an error at launch      */
+} pa_status;
+
+/* Kernel families (pa_config.kernel). */
+typedef enum {
+    PA_KERNEL_AUTO = 0,     /* library chooses                                   */
+    PA_KERNEL_GENERIC = 1,  /* plain kernel: any D <= 512, any B >= 1, any group,
+                               fp32 / fp16 / bf16; one pass, no workspace        */
+    PA_KERNEL_VALU = 2,     /* tiled kernel: D = 128, fp16 / bf16, B a power of
+                               two, groups of 1, 2, 4 or 8 query heads; 16-byte
+                               loads of whole block rows, VALU dot products     */
+    PA_KERNEL_MFMA = 3      /* grouped-query kernel: D = 128, fp16 / bf16, B a
+                               power of two, 4, 8 or 16 query heads per kv head;
+                               the group's q.K and p.V contractions on matrix
+                               cores                                             */
+} pa_kernel;
+
+/* Stages of a call (pa_config.stages, a bit mask). */
+enum {
+    PA_STAGE_PARTITIONS = 1, /* attention over each context partition           */
+    PA_STAGE_COMBINE = 2,    /* log-sum-exp merge of partitions (split plans)   */
+    PA_STAGE_ALL = 3
+};
+
+/* Optional explicit configuration; a zero-initialised struct means "auto". */
+typedef struct {
+    int kernel;           /* pa_kernel                                           */
+    int partition_tokens; /* 0: automatic.  Otherwise tokens per context
+                             partition, a positive multiple of 32.  A value at
+                             or above max_blocks * B gives a single-pass plan.   */
+    int stages;           /* 0 means PA_STAGE_ALL                                */
+} pa_config;
+
+/* The plan a call will execute (filled by pa_decode_plan). */
+typedef struct {
+    int kernel;           /* resolved pa_kernel                                  */
+    int partition_tokens; /* tokens per partition (>= max_blocks * B if single)  */
+    int max_partitions;   /* partitions per (sequence, head) the grid covers     */
+    int split;            /* 1: partial results go to the workspace and a
+                             combine stage merges them; 0: single pass          */
+    size_t workspace_bytes; /* bytes of device workspace the plan needs (0 if
+                               single pass)                                     */
+} pa_plan;
+
+/*
+ * pa_decode_plan -- resolve the kernel and context partitioning for a shape.
+ * Host-only: touches no device and launches nothing.  `cfg` may be NULL
+ * (automatic).  Returns the same validation status pa_decode_ex would for
+ * these sizes and types.
+ */
+pa_status pa_decode_plan(int S, int Hq, int Hkv, int D, int B, int NB,
+                         int max_blocks, pa_dtype dtype, pa_dtype out_dtype,
+                         const pa_config *cfg, pa_plan *plan);
+
+/*
+ * pa_decode_workspace_bytes -- device workspace pa_decode needs for this
+ * shape (the automatic plan); 0 when that plan is single pass.  Returns 0 for
+ * invalid shapes too (pa_decode then reports the error).
+ */
+size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int NB,
+                                 int max_blocks, pa_dtype dtype,
+                                 pa_dtype out_dtype);
+
+/*
+ * pa_decode -- paged decode attention with the automatic plan.
+ *
+ * scale      multiplies every dot product (usually 1 / sqrt(D)).
+ * out_dtype  dtype or PA_F32.
+ * workspace  device buffer of at least pa_decode_workspace_bytes(...) bytes,
+ *            256-byte aligned; may be NULL when that size is 0.  Its contents
+ *            need no initialisation and are scratch after the call.
+ * S = 0 is a no-op returning PA_OK.
+ *
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (e.g. D > 512,
+ * out_dtype not in {dtype, PA_F32}), PA_ERR_WORKSPACE, PA_ERR_HIP.
+ */
+pa_status pa_decode(const void *query, const void *key_cache,
+                    const void *value_cache, const int32_t *block_tables,
+                    const int32_t *seq_lens, float scale, void *out,
+                    int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                    pa_dtype dtype, pa_dtype out_dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pa_decode_ex -- as pa_decode, with an explicit configuration.
+ *
+ * cfg->kernel forces a kernel family (PA_ERR_UNSUPPORTED if it cannot run this
+ * shape or if a pointer is not 16-byte aligned); cfg->partition_tokens forces
+ * the context partition; cfg->stages runs only part of a split plan: running
+ * PA_STAGE_PARTITIONS and then PA_STAGE_COMBINE on the same stream, with the
+ * same arguments and workspace, equals one PA_STAGE_ALL call.  In a single-pass
+ * plan PA_STAGE_COMBINE alone is a no-op.
+ */
+pa_status pa_decode_ex(const void *query, const void *key_cache,
+                       const void *value_cache, const int32_t *block_tables,
+                       const int32_t *seq_lens, float scale, void *out,
+                       int S, int Hq, int Hkv, int D, int B, int NB,
+                       int max_blocks, pa_dtype dtype, pa_dtype out_dtype,
+                       const pa_config *cfg, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_DECODE_H */

@@ -1,0 +1,181 @@
+"""Python binding of libpa_decode.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+checks tensor shapes and types, passes device pointers and the current HIP
+stream, and allocates the split plan's workspace with torch when the caller
+does not bring one.  It raises if the library is not built: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa_decode.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "pa_decode.h")
+
+# pa_dtype
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+# pa_status
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
+# pa_kernel
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA = range(4)
+KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA}
+# stages
+STAGE_PARTITIONS, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
+
+_TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+
+class PaConfig(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("partition_tokens", ctypes.c_int),
+                ("stages", ctypes.c_int)]
+
+
+class PaPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("partition_tokens", ctypes.c_int),
+                ("max_partitions", ctypes.c_int), ("split", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+_INT = ctypes.c_int
+_PTR = ctypes.c_void_p
+_SHAPE = [_INT] * 7 + [_INT, _INT]       # S Hq Hkv D B NB max_blocks dtype out_dtype
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_301_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.pa_decode_plan.restype = _INT
+    lib.pa_decode_plan.argtypes = _SHAPE + [ctypes.POINTER(PaConfig), ctypes.POINTER(PaPlan)]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_workspace_bytes.argtypes = list(_SHAPE)
+    tensors = [_PTR, _PTR, _PTR, _PTR, _PTR, ctypes.c_float, _PTR]
+    lib.pa_decode.restype = _INT
+    lib.pa_decode.argtypes = tensors + _SHAPE + [_PTR, ctypes.c_size_t, _PTR]
+    lib.pa_decode_ex.restype = _INT
+    lib.pa_decode_ex.argtypes = tensors + _SHAPE + [ctypes.POINTER(PaConfig), _PTR,
+                                                    ctypes.c_size_t, _PTR]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [_INT]
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions include/pa_decode.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PaError(status, status_string(status))
+
+
+def _config(kernel="auto", partition_tokens=0, stages=0) -> PaConfig:
+    k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    return PaConfig(k, int(partition_tokens), int(stages))
+
+
+def _shape_args(query, key_cache, block_tables, out_dtype):
+    S, Hq, D = query.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D:
+        raise ValueError("query and cache head sizes differ")
+    max_blocks = block_tables.shape[1]
+    return (S, Hq, Hkv, D, B, NB, max_blocks, _TORCH_TO_PA[query.dtype], _TORCH_TO_PA[out_dtype])
+
+
+def plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype=None, *, kernel="auto",
+         partition_tokens=0, stages=0) -> dict:
+    """Resolve the plan for a shape (host only; no GPU needed)."""
+    dt = _TORCH_TO_PA.get(dtype, dtype)
+    odt = dt if out_dtype is None else _TORCH_TO_PA.get(out_dtype, out_dtype)
+    p = PaPlan()
+    cfg = _config(kernel, partition_tokens, stages)
+    _check(load().pa_decode_plan(S, Hq, Hkv, D, B, NB, max_blocks, dt, odt,
+                                 ctypes.byref(cfg), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+           block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+           out: Optional[torch.Tensor] = None, *, out_dtype: Optional[torch.dtype] = None,
+           kernel="auto", partition_tokens: int = 0, stages: int = 0,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Paged decode attention: out[S,Hq,D] from query[S,Hq,D], K/V pools
+    [NB,Hkv,B,D], block_tables[S,max_blocks] int32 and seq_lens[S] int32.
+
+    All tensors must be contiguous and on the same GPU.  Asynchronous on
+    ``stream`` (default: torch's current stream).
+    """
+    lib = load()
+    for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query, key_cache and value_cache must share one dtype")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else query.dtype
+    if out is None:
+        out = torch.empty(query.shape, dtype=out_dtype, device=query.device)
+    elif out.shape != query.shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [S,Hq,D] tensor of out_dtype")
+    shape = _shape_args(query, key_cache, block_tables, out_dtype)
+    if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
+        raise ValueError("seq_lens / block_tables do not match the batch size")
+    cfg = _config(kernel, partition_tokens, stages)
+    p = PaPlan()
+    _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
+    ws_ptr, ws_bytes = None, 0
+    if p.workspace_bytes:
+        if workspace is None:
+            workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib.pa_decode_ex(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                            block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
+                            out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr, ws_bytes, st))
+    return out
+
+
+def decode_workload(w, out_dtype=None, **kw) -> torch.Tensor:
+    """decode() on a ``workloads.Workload``."""
+    return decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
+                  out_dtype=out_dtype, **kw)

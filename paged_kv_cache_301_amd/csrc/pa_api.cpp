@@ -1,0 +1,234 @@
+// pa_api.cpp -- the C ABI of libpa_decode.so: argument validation, planning
+// (kernel family, context partitioning, workspace layout) and launches.
+//
+// Validation and planning are plain host code with no HIP calls, so they run
+// (and are tested) on machines without a GPU.
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::Args;
+
+// Tokens per context partition when the caller does not choose.
+constexpr int kAutoPartitionTokens = 256;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool valid_dtype(int d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+
+pa_status validate_shape(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                         pa_dtype dtype, pa_dtype out_dtype) {
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || max_blocks < 0)
+        return PA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return PA_ERR_SHAPE;
+    if (S > 65535 || Hq > 65535) return PA_ERR_SHAPE;              // launch grid limits
+    if ((long long)max_blocks * B > INT_MAX) return PA_ERR_SHAPE;  // token index is int32
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PA_ERR_UNSUPPORTED;
+    if (out_dtype != dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+    if (D > 512) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+bool supports_valu(int Hq, int Hkv, int D, int B, pa_dtype dt) {
+    const int G = Hq / Hkv;
+    return D == 128 && (dt == PA_F16 || dt == PA_BF16) && is_pow2(B) &&
+           (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+bool supports_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
+    const int G = Hq / Hkv;
+    return D == 128 && (dt == PA_F16 || dt == PA_BF16) && is_pow2(B) &&
+           (G == 4 || G == 8 || G == 16);
+}
+
+// Largest partition whose block-table slice fits the LDS copy (kernels that
+// stage the table: VALU with B % 4 != 0, MFMA with B % 16 != 0).
+long long table_cap(int kernel, int B) {
+    const bool staged = (kernel == PA_KERNEL_VALU && B % 4 != 0) ||
+                        (kernel == PA_KERNEL_MFMA && B % 16 != 0);
+    return staged ? 1024LL * B : (long long)INT_MAX;
+}
+
+pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                    pa_dtype dtype, pa_dtype out_dtype, const pa_config *cfg, pa_plan *plan) {
+    pa_status st = validate_shape(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype);
+    if (st != PA_OK) return st;
+    int kernel = cfg ? cfg->kernel : PA_KERNEL_AUTO;
+    const int req = cfg ? cfg->partition_tokens : 0;
+    if (req < 0 || (req > 0 && req % pa::kTileTokens != 0)) return PA_ERR_SHAPE;
+    if (cfg && (cfg->stages < 0 || cfg->stages > PA_STAGE_ALL)) return PA_ERR_SHAPE;
+
+    switch (kernel) {
+    case PA_KERNEL_AUTO:
+        kernel = supports_mfma(Hq, Hkv, D, B, dtype)   ? PA_KERNEL_MFMA
+                 : supports_valu(Hq, Hkv, D, B, dtype) ? PA_KERNEL_VALU
+                                                       : PA_KERNEL_GENERIC;
+        break;
+    case PA_KERNEL_GENERIC:
+        break;
+    case PA_KERNEL_VALU:
+        if (!supports_valu(Hq, Hkv, D, B, dtype)) return PA_ERR_UNSUPPORTED;
+        break;
+    case PA_KERNEL_MFMA:
+        if (!supports_mfma(Hq, Hkv, D, B, dtype)) return PA_ERR_UNSUPPORTED;
+        break;
+    default:
+        return PA_ERR_UNSUPPORTED;
+    }
+
+    const long long max_ctx = (long long)max_blocks * B;
+    pa_plan p{};
+    p.kernel = kernel;
+    if (kernel == PA_KERNEL_GENERIC) {
+        // one pass over the whole context; no workspace
+        p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
+        p.max_partitions = 1;
+        p.split = 0;
+    } else {
+        const long long cap = table_cap(kernel, B);
+        long long part = req > 0 ? req : kAutoPartitionTokens;
+        if (part >= max_ctx) {   // single pass: one partition covers any context
+            part = ((max_ctx > 0 ? max_ctx : 1) + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;
+        }
+        if (part > cap) part = cap / pa::kTileTokens * pa::kTileTokens;
+        if (part > INT_MAX) part = INT_MAX / pa::kTileTokens * pa::kTileTokens;
+        const long long parts = max_ctx > 0 ? (max_ctx + part - 1) / part : 1;
+        if (parts > INT_MAX) return PA_ERR_SHAPE;
+        p.partition_tokens = (int)part;
+        p.max_partitions = (int)parts;
+        p.split = parts > 1 ? 1 : 0;
+    }
+    if (p.split) {
+        const size_t rows = (size_t)S * Hq * p.max_partitions;
+        p.workspace_bytes = align256(rows * D * sizeof(float)) + 2 * align256(rows * sizeof(float));
+    }
+    *plan = p;
+    return PA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                         pa_dtype dtype, pa_dtype out_dtype, const pa_config *cfg,
+                         pa_plan *plan) {
+    if (!plan) return PA_ERR_NULL;
+    return make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, cfg, plan);
+}
+
+size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                                 pa_dtype dtype, pa_dtype out_dtype) {
+    pa_plan p;
+    if (make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, nullptr, &p) != PA_OK)
+        return 0;
+    return p.workspace_bytes;
+}
+
+pa_status pa_decode_ex(const void *query, const void *key_cache, const void *value_cache,
+                       const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                       void *out, int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                       pa_dtype dtype, pa_dtype out_dtype, const pa_config *cfg,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    pa_plan plan;
+    pa_status st = make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, cfg, &plan);
+    if (st != PA_OK) return st;
+    if (S == 0) return PA_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !seq_lens || !out)
+        return PA_ERR_NULL;
+
+    if (plan.kernel != PA_KERNEL_GENERIC &&
+        !(aligned16(query) && aligned16(key_cache) && aligned16(value_cache) && aligned16(out))) {
+        if (cfg && cfg->kernel != PA_KERNEL_AUTO) return PA_ERR_UNSUPPORTED;
+        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0};
+        st = make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, &gen, &plan);
+        if (st != PA_OK) return st;
+    }
+    const int stages = (cfg && cfg->stages) ? cfg->stages : PA_STAGE_ALL;
+
+    Args a;
+    std::memset(&a, 0, sizeof a);
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.scale_log2 = scale * 1.4426950408889634f;   // log2(e): exp(x) = 2^(x log2 e)
+    a.S = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.B = B;
+    a.NB = NB;
+    a.max_blocks = max_blocks;
+    a.log2B = is_pow2(B) ? ilog2(B) : -1;
+    a.part_tokens = plan.partition_tokens;
+    a.max_parts = plan.max_partitions;
+    a.split = plan.split;
+    if (plan.split) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+            workspace_bytes < plan.workspace_bytes)
+            return PA_ERR_WORKSPACE;
+        const size_t rows = (size_t)S * Hq * plan.max_partitions;
+        char *ws = static_cast<char *>(workspace);
+        a.part_o = reinterpret_cast<float *>(ws);
+        a.part_m = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)));
+        a.part_l = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)) +
+                                             align256(rows * sizeof(float)));
+    }
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t err = hipSuccess;
+    if (stages & PA_STAGE_PARTITIONS) {
+        switch (plan.kernel) {
+        case PA_KERNEL_GENERIC: err = pa::launch_generic(a, dtype, out_dtype, hs); break;
+        case PA_KERNEL_VALU: err = pa::launch_valu(a, dtype, out_dtype, hs); break;
+        case PA_KERNEL_MFMA: err = pa::launch_mfma(a, dtype, out_dtype, hs); break;
+        default: return PA_ERR_UNSUPPORTED;
+        }
+        if (err != hipSuccess) return PA_ERR_HIP;
+    }
+    if (plan.split && (stages & PA_STAGE_COMBINE)) {
+        err = pa::launch_combine(a, out_dtype, hs);
+        if (err != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
+}
+
+pa_status pa_decode(const void *query, const void *key_cache, const void *value_cache,
+                    const int32_t *block_tables, const int32_t *seq_lens, float scale, void *out,
+                    int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks, pa_dtype dtype,
+                    pa_dtype out_dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return pa_decode_ex(query, key_cache, value_cache, block_tables, seq_lens, scale, out, S, Hq,
+                        Hkv, D, B, NB, max_blocks, dtype, out_dtype, nullptr, workspace,
+                        workspace_bytes, stream);
+}
+
+const char *pa_status_string(pa_status status) {
+    switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid sizes";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape, type or kernel not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "unknown pa_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// pa_internal.h -- argument block and launcher declarations shared by the
+// host entry points (pa_api.cpp) and the kernel files.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#include "pa_decode.h"
+
+namespace pa {
+
+// Everything one launch needs, passed to kernels by value (kernarg segment).
+struct Args {
+    const void *query;        // [S][Hq][D]
+    const void *key_cache;    // [NB][Hkv][B][D]
+    const void *value_cache;  // [NB][Hkv][B][D]
+    const int32_t *block_tables;  // [S][max_blocks]
+    const int32_t *seq_lens;      // [S]
+    void *out;                // [S][Hq][D] (out dtype)
+    float *part_o;            // [S][Hq][max_parts][D]   split plans only
+    float *part_m;            // [S][Hq][max_parts]      running max, log2 units
+    float *part_l;            // [S][Hq][max_parts]      sum of weights
+    float scale_log2;         // scale * log2(e): scores live in exp2 units
+    int S, Hq, Hkv, D, B, NB, max_blocks;
+    int log2B;                // log2(B) when B is a power of two, else -1
+    int part_tokens;          // tokens per context partition
+    int max_parts;            // partitions per (s, head) in the grid
+    int split;                // 1: write partials, 0: write final output
+};
+
+// Launchers return hipErrorInvalidValue when no instantiation covers the
+// requested shape / types (the host checks support before calling).
+hipError_t launch_generic(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
+hipError_t launch_valu(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
+hipError_t launch_mfma(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
+hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st);
+
+// Tokens one loop iteration of the tiled kernels covers; partitions are
+// multiples of this.
+constexpr int kTileTokens = 32;
+
+}  // namespace pa

@@ -1,0 +1,307 @@
+// pa_mfma.hip -- grouped-query paged decode attention on the matrix cores.
+//
+// When G = Hq / Hkv query heads share one kv head, each K / V tile read from
+// HBM serves all G heads, so the two contractions per tile are small dense
+// matrix products:
+//     S^T [tokens x heads] = K [tokens x D]   . Q^T [D x heads]
+//     O^T [D x heads]     += V^T [D x tokens] . P^T [tokens x heads]
+// Both run on v_mfma_f32_16x16x32_{bf16,f16} with the head group padded to 16
+// columns.  One wave64 handles one (sequence, kv head, context partition); an
+// iteration covers 32 tokens (two 16-row score tiles, one 32-deep P.V step).
+//
+// Operand layouts (lane = 16 * g + i):
+//  * QK, A = K rows: lane reads token i of a 16-token sub-tile, elements
+//    8g + 32kk .. +7 of the row (one 16-byte load per kk).  B = Q^T: lane holds
+//    q[head i] at the same elements, loaded once.
+//  * The result lane holds S^T[4g + r][i], r = 0..3: scores of four tokens for
+//    head i.  The two sub-tiles give the lane tokens {4g+r} and {16+4g+r}.
+//  * PV, B = P^T: lane holds P[head i] at exactly those eight tokens, so the
+//    contraction index k = (g, j) maps to token 4g + j (j < 4) or
+//    16 + 4g + j - 4 (j >= 4) and no probability moves between lanes.
+//  * PV, A = V^T: lane holds V[token(g, j)][16n + i] for d-chunk n.  V arrives
+//    token-major, so it is staged through LDS: whole 1 KB rows are written
+//    with 16-byte stores (16-byte chunks XOR-swizzled by row so the column
+//    reads below are bank-conflict free) and read back one column element at
+//    a time.
+//  * The PV result lane holds O^T[16n + 4g + r][i]: four consecutive output
+//    elements of head i, and the softmax rescale factor of head i is lane-local.
+//
+// Softmax is online over iterations (running max per head, made uniform over
+// the four lane groups by two cross-lane max steps).  The probabilities enter
+// the matrix core as a two-term split in the input type (p = hi + lo, both
+// rounded to bf16 / fp16), with fp32 accumulation: one rounding of p to 16
+// bits would cost up to 2^-9 (bf16) or 2^-12 (fp16) relative per weight.
+#include "pa_internal.h"
+#include "pa_device.h"
+#include "pa_table.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kD = 128;
+
+template <typename T> struct Mfma;
+template <> struct Mfma<__bf16> {
+    using Vec = bf16x8;
+    __device__ static f32x4 mma(Vec a, Vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<_Float16> {
+    using Vec = f16x8;
+    __device__ static f32x4 mma(Vec a, Vec b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Two-term split of the probabilities for the 16-bit matrix-core operand:
+// hi = round(p), lo = round(p - hi), so hi + lo carries 2 * (mantissa + 1)
+// bits of p and the P.V product keeps fp32-level accuracy.
+template <typename T, typename Vec>
+__device__ __forceinline__ void split_probs(const float (&p)[8], Vec &hi, Vec &lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const T h = (T)p[j];
+        hi[j] = h;
+        lo[j] = (T)(p[j] - (float)h);
+    }
+}
+
+struct MfmaTile {
+    uint4 k[2][4];   // [sub-tile][kk]
+    uint4 v[8];      // token 4k + g, chunk i
+};
+
+// SCALAR_K: the 16 rows of a K sub-tile share one block (B % 16 == 0).
+// SCALAR_V: the 4 rows of a V load share one block (B % 4 == 0).
+template <bool SCALAR_K, bool SCALAR_V>
+struct MfmaCtx {
+    const char *kbase;     // key_cache + kv head offset (bytes)
+    const char *vbase;     // value_cache + kv head offset + 16 * i (bytes)
+    size_t block_bytes;
+    int bmask;
+    int t_end;
+    int g, i;
+    TableView tv;
+    const int32_t *tbl;
+
+    __device__ __forceinline__ void load(MfmaTile &tile, int t0) const {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = min(t0 + 16 * u + i, t_end - 1);
+            const int phys = phys_block<SCALAR_K>(tv, tbl, t);
+            const char *row = kbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2) + 16 * g;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) tile.k[u][kk] = *reinterpret_cast<const uint4 *>(row + 64 * kk);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int t = min(t0 + 4 * k + g, t_end - 1);
+            const int phys = phys_block<SCALAR_V>(tv, tbl, t);
+            tile.v[k] = *reinterpret_cast<const uint4 *>(
+                vbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2));
+        }
+    }
+};
+
+// LDS image of one iteration's V: 32 token rows x 16 chunks of 16 bytes, the
+// chunk index XORed with 2 * ((row / 4) % 4).
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (2 * ((row >> 2) & 3)); }
+
+template <typename T, int G>
+struct MfmaState {
+    f32x4 o[8];   // O^T, d-chunk n: rows 16n + 4g + r, column = head i
+    float m;      // running max of head i (exp2 units), uniform over g
+    float l;      // this lane's share of head i's weight sum
+};
+
+template <typename T, int G>
+__device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile &tile,
+                                             const typename Mfma<T>::Vec (&qf)[4],
+                                             uint4 *vlds, int t0, int t_end, int g, int i,
+                                             float scale_log2) {
+    using M = Mfma<T>;
+    using Vec = typename M::Vec;
+    // V rows to LDS (row 4k + g, swizzled chunk)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) vlds[(4 * k + g) * 16 + swz_chunk(4 * k + g, i)] = tile.v[k];
+
+    // scores
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = M::mma(bitcast<Vec>(tile.k[u][kk]), qf[kk], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            x[4 * u + r] = (t0 + 16 * u + 4 * g + r < t_end) ? acc[r] * scale_log2 : kNegInf;
+    }
+    float mt = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    mt = fmaxf(mt, shfl_xor(mt, 16));
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float mn = fmaxf(st.m, mt);     // finite: token t0 is valid
+    const float alpha = fast_exp2(st.m - mn);
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p[j] = fast_exp2(x[j] - mn);
+        ps += p[j];
+    }
+    st.l = st.l * alpha + ps;
+    st.m = mn;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+    Vec phi, plo;
+    split_probs<T>(p, phi, plo);
+
+    __syncthreads();   // V rows visible to every lane
+    const u16 *vl = reinterpret_cast<const u16 *>(vlds);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        // column 16n + i of rows 4g + j (j < 4) and 16 + 4g + j - 4; the swizzle
+        // term of all eight rows is 2g
+        const int col = ((((2 * n + (i >> 3)) ^ (2 * g)) * 16) >> 1) + (i & 7);
+        const int rbase = (4 * g) * 128;
+        Vec va;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row_off = (j < 4 ? j : 16 + j - 4) * 128;
+            va[j] = bitcast<T>(vl[rbase + row_off + col]);
+        }
+        st.o[n] = M::mma(va, phi, st.o[n]);
+        st.o[n] = M::mma(va, plo, st.o[n]);
+    }
+    __syncthreads();   // reads done before the next iteration overwrites LDS
+}
+
+template <typename T, typename OutT, int G, bool SCALAR_K, bool SCALAR_V>
+__global__ __launch_bounds__(64) void mfma_kernel(Args a) {
+    using Vec = typename Mfma<T>::Vec;
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int s = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int i = lane & 15;
+    const int g = lane >> 4;
+
+    const int L = a.seq_lens[s];
+    const int t_begin = p * a.part_tokens;
+    if (p > 0 && t_begin >= L) return;
+    const int t_end = min(L, t_begin + a.part_tokens);
+    const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+
+    __shared__ uint4 vlds[32 * 16];
+    __shared__ int32_t tbl[(SCALAR_K && SCALAR_V) ? 1 : kTableLds];
+
+    // Q^T fragments; columns past the group are zero
+    Vec qf[4];
+    const bool head_ok = i < G;
+    const T *qrow = static_cast<const T *>(a.query) + ((size_t)s * a.Hq + kvh * G + (head_ok ? i : 0)) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        uint4 w = *reinterpret_cast<const uint4 *>(qrow + 8 * g + 32 * kk);
+        if (!head_ok) w = make_uint4(0, 0, 0, 0);
+        qf[kk] = bitcast<Vec>(w);
+    }
+
+    MfmaState<T, G> st;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.l = 0.f;
+
+    if (L > 0) {
+        MfmaCtx<SCALAR_K, SCALAR_V> ctx;
+        const size_t head_bytes = (size_t)a.B * kD * 2;
+        ctx.kbase = static_cast<const char *>(a.key_cache) + kvh * head_bytes;
+        ctx.vbase = static_cast<const char *>(a.value_cache) + kvh * head_bytes + 16 * i;
+        ctx.block_bytes = (size_t)a.Hkv * head_bytes;
+        ctx.bmask = a.B - 1;
+        ctx.t_end = t_end;
+        ctx.g = g;
+        ctx.i = i;
+        ctx.tv.row = a.block_tables + (size_t)s * a.max_blocks;
+        ctx.tv.lb = a.log2B;
+        ctx.tv.j0 = t_begin >> a.log2B;
+        ctx.tbl = tbl;
+        if constexpr (!(SCALAR_K && SCALAR_V)) {
+            stage_table(tbl, ctx.tv, t_begin, t_end, lane, 64);
+            __syncthreads();
+        }
+
+        const int niter = (t_end - t_begin + 31) >> 5;
+        MfmaTile ta, tb;
+        ctx.load(ta, t_begin);
+        for (int it = 0; it < niter; it += 2) {
+            const int t0 = t_begin + 32 * it;
+            ctx.load(tb, t0 + 32);
+            mfma_compute<T, G>(st, ta, qf, vlds, t0, t_end, g, i, a.scale_log2);
+            ctx.load(ta, t0 + 64);
+            if (it + 1 < niter) mfma_compute<T, G>(st, tb, qf, vlds, t0 + 32, t_end, g, i, a.scale_log2);
+        }
+        st.l += shfl_xor(st.l, 16);
+        st.l += shfl_xor(st.l, 32);
+    }
+
+    if (!head_ok) return;
+    const int head = kvh * G + i;
+    if (nparts <= 1) {
+        const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                store_elem<OutT>(a.out, ((size_t)s * a.Hq + head) * kD + 16 * n + 4 * g + r, st.o[n][r] * inv);
+        }
+    } else {
+        const size_t idx = ((size_t)s * a.Hq + head) * a.max_parts + p;
+        float *dst = a.part_o + idx * kD;
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            *reinterpret_cast<float4 *>(dst + 16 * n + 4 * g) =
+                make_float4(st.o[n][0], st.o[n][1], st.o[n][2], st.o[n][3]);
+        if (g == 0) {
+            a.part_m[idx] = st.m;
+            a.part_l[idx] = st.l;
+        }
+    }
+}
+
+template <typename T, typename OutT, int G>
+hipError_t launch_g(const Args &a, hipStream_t st) {
+    dim3 grid(a.max_parts, a.Hkv, a.S);
+    if (a.B % 16 == 0)
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, true>), grid, dim3(64), 0, st, a);
+    else if (a.B % 4 == 0)
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, true>), grid, dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, false>), grid, dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, typename OutT>
+hipError_t launch_t(const Args &a, hipStream_t st) {
+    switch (a.Hq / a.Hkv) {
+    case 4: return launch_g<T, OutT, 4>(a, st);
+    case 8: return launch_g<T, OutT, 8>(a, st);
+    case 16: return launch_g<T, OutT, 16>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_mfma(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st) {
+    if (a.D != kD || a.log2B < 0) return hipErrorInvalidValue;
+    const bool f32out = (odt == PA_F32);
+    if (dt == PA_F16) return f32out ? launch_t<_Float16, float>(a, st) : launch_t<_Float16, _Float16>(a, st);
+    if (dt == PA_BF16) return f32out ? launch_t<__bf16, float>(a, st) : launch_t<__bf16, __bf16>(a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

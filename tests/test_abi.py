@@ -1,0 +1,111 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+validates arguments and plans calls.  No compute entry point launches here:
+every call below is rejected by host-side validation before any HIP call, or
+is the S = 0 no-op, or is the host-only planner."""
+import ctypes
+
+import pytest
+import torch
+
+from paged_kv_cache_301_amd import binding as b
+
+F16, BF16, F32 = b.PA_F16, b.PA_BF16, b.PA_F32
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = b.header_functions()
+    assert set(names) >= {"pa_decode", "pa_decode_ex", "pa_decode_plan",
+                          "pa_decode_workspace_bytes", "pa_status_string"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/pa_decode.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.pa_status_string(s).decode().startswith("PA_")
+    assert b"unknown" in lib.pa_status_string(99)
+
+
+def _call(lib, *, S=2, Hq=4, Hkv=2, D=128, B=16, NB=8, mb=4, dt=BF16, odt=BF16,
+          null=(), ws=None, ws_bytes=0, cfg=None):
+    fake = 1 << 20   # never dereferenced: every case here fails validation first
+    ptrs = [None if i in null else fake for i in range(7)]
+    return lib.pa_decode_ex(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], 0.1, ptrs[5],
+                            S, Hq, Hkv, D, B, NB, mb, dt, odt,
+                            ctypes.byref(cfg) if cfg else None, ws, ws_bytes, None)
+
+
+def test_validation_errors(lib):
+    assert _call(lib, Hq=6, Hkv=4) == b.PA_ERR_SHAPE
+    assert _call(lib, S=-1) == b.PA_ERR_SHAPE
+    assert _call(lib, D=0) == b.PA_ERR_SHAPE
+    assert _call(lib, B=0) == b.PA_ERR_SHAPE
+    assert _call(lib, NB=0) == b.PA_ERR_SHAPE
+    assert _call(lib, mb=-1) == b.PA_ERR_SHAPE
+    assert _call(lib, mb=1 << 20, B=1 << 12) == b.PA_ERR_SHAPE       # tokens overflow int32
+    assert _call(lib, D=513) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, dt=7) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, dt=F16, odt=BF16) == b.PA_ERR_UNSUPPORTED
+    for i in range(6):
+        assert _call(lib, null=(i,)) == b.PA_ERR_NULL
+    # split plan without / with a short workspace
+    cfg = b.PaConfig(b.KERNEL_AUTO, 32, 0)
+    assert _call(lib, cfg=cfg) == b.PA_ERR_WORKSPACE
+    assert _call(lib, cfg=cfg, ws=1 << 20, ws_bytes=16) == b.PA_ERR_WORKSPACE
+    # forced kernel that cannot run the shape
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_MFMA, 0, 0), Hq=4, Hkv=4) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_VALU, 0, 0), D=64) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, cfg=b.PaConfig(9, 0, 0)) == b.PA_ERR_UNSUPPORTED
+    # partition not a multiple of 32
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_AUTO, 48, 0)) == b.PA_ERR_SHAPE
+
+
+def test_empty_batch_is_noop(lib):
+    assert _call(lib, S=0, null=(0, 1, 2, 3, 4, 5)) == b.PA_OK
+
+
+def test_plans():
+    p = b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16)
+    assert p["kernel"] == b.KERNEL_VALU and p["split"] == 1
+    assert p["max_partitions"] * p["partition_tokens"] >= 256 * 16
+    assert p["workspace_bytes"] >= 64 * 32 * p["max_partitions"] * (128 + 2) * 4
+    p = b.plan(128, 64, 8, 128, 16, 100, 512, torch.bfloat16)
+    assert p["kernel"] == b.KERNEL_MFMA
+    p = b.plan(1, 1, 1, 2, 2, 8, 3, torch.float32)
+    assert p["kernel"] == b.KERNEL_GENERIC and p["split"] == 0 and p["workspace_bytes"] == 0
+    # short contexts: single pass
+    p = b.plan(8, 32, 32, 128, 16, 100, 8, torch.float16)
+    assert p["split"] == 0 and p["partition_tokens"] >= 128 and p["workspace_bytes"] == 0
+    # forcing a partition size; a partition at least the context gives one pass
+    p = b.plan(8, 32, 32, 128, 16, 100, 8, torch.float16, partition_tokens=32)
+    assert p["split"] == 1 and p["max_partitions"] == 4
+    p = b.plan(8, 32, 32, 128, 16, 100, 8, torch.float16, partition_tokens=4096)
+    assert p["split"] == 0
+    # block size 1 with the matrix-core kernel: the table slice fits LDS
+    p = b.plan(16, 32, 8, 128, 1, 10, 32768, torch.bfloat16, partition_tokens=4096)
+    assert p["partition_tokens"] <= 1024
+    # generic ignores partitioning
+    p = b.plan(2, 4, 2, 96, 3, 10, 50, torch.bfloat16)
+    assert p["kernel"] == b.KERNEL_GENERIC and p["split"] == 0
+
+
+def test_workspace_bytes_matches_plan(lib):
+    for args in [(64, 32, 32, 128, 16, 15360, 256, BF16, BF16),
+                 (16, 32, 8, 128, 1, 10, 32768, BF16, F32),
+                 (1, 1, 1, 2, 2, 8, 3, F32, F32)]:
+        p = b.plan(*args)
+        assert lib.pa_decode_workspace_bytes(*args) == p["workspace_bytes"]
+    assert lib.pa_decode_workspace_bytes(1, 3, 2, 128, 16, 8, 4, BF16, BF16) == 0   # invalid
+
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 1, 2)
+    kc = torch.zeros(4, 1, 2, 2)
+    with pytest.raises(ValueError):
+        b.decode(q, kc, kc, torch.zeros(1, 2, dtype=torch.int32),
+                 torch.ones(1, dtype=torch.int32), 1.0)
