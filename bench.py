@@ -42,7 +42,39 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--print-source-sha", action="store_true",
+                    help="print the kernel-source hash used to match counter records, then exit")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one plain device-to-device copy of this many MiB "
+                         "(a known-size reference for hardware byte counters)")
     return ap.parse_args()
+
+
+def source_sha256() -> str:
+    """Hash of the kernel sources (ties hardware-counter records to a build)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_301_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, workload: str, block_size: int):
+    """HBM bytes per launch from a rocprofv3 --pmc summary under profiles/,
+    if one was recorded for these exact kernel sources; else None."""
+    import glob
+    import re
+    sha = source_sha256()
+    pat = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) "
+                     r"source_sha256=([0-9a-f]+) read_bytes=(\d+) write_bytes=(\d+)")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for m in pat.finditer(open(path).read()):
+            if (m.group(1), m.group(2), int(m.group(3)), m.group(4)) == (kernel, workload, block_size, sha):
+                return int(m.group(5)) + int(m.group(6))
+    return None
 
 
 def cpu_baseline(w, target_s):
@@ -78,6 +110,9 @@ def cpu_baseline(w, target_s):
 
 def main():
     args = parse()
+    if args.print_source_sha:
+        print(source_sha256())
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the hot path needs no cross-GPU exchange; see the sharding note in the design doc)",
@@ -127,6 +162,14 @@ def main():
         if evs is not None:
             evs[2].record(stream)
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -174,7 +217,8 @@ def main():
                       "combine": round(float(comb_ms.mean()) * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": f"pa_{kname}_partitions",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"pa_{kname}_partitions", args.workload, w.B)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

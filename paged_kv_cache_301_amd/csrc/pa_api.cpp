@@ -13,8 +13,23 @@ namespace {
 
 using pa::Args;
 
-// Tokens per context partition when the caller does not choose.
-constexpr int kAutoPartitionTokens = 256;
+// Automatic partition size: kAutoPartitionMax tokens, halved (down to
+// kAutoPartitionMin) while the grid would hold fewer than kAutoMinItems
+// (sequence, kv head, partition) items -- small batches need shorter
+// partitions to occupy 256 CUs; large ones amortise the combine pass.
+constexpr int kAutoPartitionMax = 512;
+constexpr int kAutoPartitionMin = 64;
+constexpr long long kAutoMinItems = 8192;
+constexpr long long kAutoSinglePass = 256;
+
+long long auto_partition(int S, int Hkv, long long max_ctx) {
+    if (max_ctx <= kAutoSinglePass) return max_ctx;   // short contexts: one pass
+    long long part = kAutoPartitionMax;
+    while (part > kAutoPartitionMin &&
+           (long long)S * Hkv * ((max_ctx + part - 1) / part) < kAutoMinItems)
+        part /= 2;
+    return part;
+}
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -34,6 +49,7 @@ pa_status validate_shape(int S, int Hq, int Hkv, int D, int B, int NB, int max_b
         return PA_ERR_SHAPE;
     if (Hq % Hkv != 0) return PA_ERR_SHAPE;
     if (S > 65535 || Hq > 65535) return PA_ERR_SHAPE;              // launch grid limits
+    if ((long long)S * Hq > INT_MAX) return PA_ERR_SHAPE;
     if ((long long)max_blocks * B > INT_MAX) return PA_ERR_SHAPE;  // token index is int32
     if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return PA_ERR_UNSUPPORTED;
     if (out_dtype != dtype && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
@@ -90,25 +106,35 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
 
     const long long max_ctx = (long long)max_blocks * B;
     pa_plan p{};
-    p.kernel = kernel;
-    if (kernel == PA_KERNEL_GENERIC) {
-        // one pass over the whole context; no workspace
-        p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
-        p.max_partitions = 1;
-        p.split = 0;
-    } else {
+    if (kernel != PA_KERNEL_GENERIC) {
         const long long cap = table_cap(kernel, B);
-        long long part = req > 0 ? req : kAutoPartitionTokens;
+        long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx);
         if (part >= max_ctx) {   // single pass: one partition covers any context
             part = ((max_ctx > 0 ? max_ctx : 1) + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;
         }
+        // the partition index is a grid dimension (at most kMaxPartitions)
+        const long long min_part = (max_ctx + pa::kMaxPartitions - 1) / pa::kMaxPartitions;
+        if (part < min_part) part = (min_part + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;
         if (part > cap) part = cap / pa::kTileTokens * pa::kTileTokens;
         if (part > INT_MAX) part = INT_MAX / pa::kTileTokens * pa::kTileTokens;
         const long long parts = max_ctx > 0 ? (max_ctx + part - 1) / part : 1;
-        if (parts > INT_MAX) return PA_ERR_SHAPE;
-        p.partition_tokens = (int)part;
-        p.max_partitions = (int)parts;
-        p.split = parts > 1 ? 1 : 0;
+        if (parts <= pa::kMaxPartitions) {
+            p.kernel = kernel;
+            p.partition_tokens = (int)part;
+            p.max_partitions = (int)parts;
+            p.split = parts > 1 ? 1 : 0;
+        } else if (cfg && cfg->kernel != PA_KERNEL_AUTO) {
+            return PA_ERR_UNSUPPORTED;   // context too long for this kernel's table staging
+        } else {
+            kernel = PA_KERNEL_GENERIC;
+        }
+    }
+    if (kernel == PA_KERNEL_GENERIC) {
+        // one pass over the whole context; no workspace
+        p.kernel = kernel;
+        p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
+        p.max_partitions = 1;
+        p.split = 0;
     }
     if (p.split) {
         const size_t rows = (size_t)S * Hq * p.max_partitions;

@@ -10,9 +10,10 @@
 // buffer).  Sequences that fit one partition were written directly by the
 // partition kernel and are skipped here.
 //
-// One wave64 per (sequence, head): lanes first own partitions (max and
-// weights, staged in LDS 64 at a time), then own head dimensions for the
-// weighted sum of the o_p rows.
+// One 256-thread work-group per (sequence, head): thread t owns output
+// columns 4 (t % 32) .. +3 and partitions t / 32, t / 32 + 8, ..., so every
+// partial row is read with full-width 16-byte loads and all partitions are in
+// flight at once; the eight partial sums meet in LDS.
 #include "pa_internal.h"
 #include "pa_device.h"
 
@@ -20,14 +21,16 @@ namespace pa {
 
 namespace {
 
-constexpr int kMaxD = 512;
+constexpr int kD = 128;
+constexpr int kThreads = 256;
+constexpr int kCols = kD / 4;                 // float4 columns per row
+constexpr int kGroups = kThreads / kCols;     // partitions handled in parallel
 
 template <typename OutT>
-__global__ __launch_bounds__(64) void combine_kernel(Args a) {
+__global__ __launch_bounds__(kThreads) void combine_kernel(Args a) {
     const int h = blockIdx.x;
     const int s = blockIdx.y;
-    const int lane = threadIdx.x;
-    const int D = a.D;
+    const int t = threadIdx.x;
     const int L = a.seq_lens[s];
     const int np = (L + a.part_tokens - 1) / a.part_tokens;
     if (np <= 1) return;
@@ -35,57 +38,65 @@ __global__ __launch_bounds__(64) void combine_kernel(Args a) {
     const size_t row = (size_t)s * a.Hq + h;
     const float *pm = a.part_m + row * a.max_parts;
     const float *pl = a.part_l + row * a.max_parts;
-    const float *po = a.part_o + row * a.max_parts * D;
+    const float4 *po = reinterpret_cast<const float4 *>(a.part_o + row * a.max_parts * kD);
 
+    __shared__ float red[kThreads / 64];
+    __shared__ float4 acc_s[kGroups][kCols];
+    __shared__ float z_s[kGroups];
+
+    // M = max over partitions
     float M = kNegInf;
-    for (int p = lane; p < np; p += 64) M = fmaxf(M, pm[p]);
+    for (int p = t; p < np; p += kThreads) M = fmaxf(M, pm[p]);
     M = wave_max(M);
+    if ((t & 63) == 0) red[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-    __shared__ float w_s[64];
-    float acc[kMaxD / 64];
+    const int c = t % kCols;
+    const int grp = t / kCols;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float z = 0.f;
+    for (int p = grp; p < np; p += kGroups) {
+        const float w = fast_exp2(pm[p] - M);
+        const float4 o = po[(size_t)p * kCols + c];
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
+        acc.z = fmaf(w, o.z, acc.z);
+        acc.w = fmaf(w, o.w, acc.w);
+        z = fmaf(w, pl[p], z);
+    }
+    acc_s[grp][c] = acc;
+    if (c == 0) z_s[grp] = z;
+    __syncthreads();
+    if (grp != 0) return;
 #pragma unroll
-    for (int k = 0; k < kMaxD / 64; ++k) acc[k] = 0.f;
+    for (int g = 1; g < kGroups; ++g) {
+        const float4 o = acc_s[g][c];
+        acc.x += o.x;
+        acc.y += o.y;
+        acc.z += o.z;
+        acc.w += o.w;
+    }
     float Z = 0.f;
-    for (int p0 = 0; p0 < np; p0 += 64) {
-        const int p = p0 + lane;
-        float w = 0.f;
-        if (p < np) {
-            w = fast_exp2(pm[p] - M);
-            Z += w * pl[p];
-        }
-        w_s[lane] = w;
-        __syncthreads();
-        const int n = min(64, np - p0);
 #pragma unroll
-        for (int k = 0; k < kMaxD / 64; ++k) {
-            const int d = lane + 64 * k;
-            if (d < D) {
-                float sum = acc[k];
-#pragma unroll 8
-                for (int j = 0; j < n; ++j) sum = fmaf(w_s[j], po[(size_t)(p0 + j) * D + d], sum);
-                acc[k] = sum;
-            }
-        }
-        __syncthreads();
-    }
-    Z = wave_sum(Z);
+    for (int g = 0; g < kGroups; ++g) Z += z_s[g];
     const float inv = 1.f / Z;
-#pragma unroll
-    for (int k = 0; k < kMaxD / 64; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) store_elem<OutT>(a.out, row * D + d, acc[k] * inv);
-    }
+    const size_t base = row * kD + 4 * c;
+    store_elem<OutT>(a.out, base + 0, acc.x * inv);
+    store_elem<OutT>(a.out, base + 1, acc.y * inv);
+    store_elem<OutT>(a.out, base + 2, acc.z * inv);
+    store_elem<OutT>(a.out, base + 3, acc.w * inv);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st) {
-    if (a.D > kMaxD) return hipErrorInvalidValue;
+    if (a.D != kD) return hipErrorInvalidValue;
     dim3 grid(a.Hq, a.S);
     switch (odt) {
-    case PA_F32: hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(64), 0, st, a); break;
-    case PA_F16: hipLaunchKernelGGL(combine_kernel<_Float16>, grid, dim3(64), 0, st, a); break;
-    case PA_BF16: hipLaunchKernelGGL(combine_kernel<__bf16>, grid, dim3(64), 0, st, a); break;
+    case PA_F32: hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, st, a); break;
+    case PA_F16: hipLaunchKernelGGL(combine_kernel<_Float16>, grid, dim3(kThreads), 0, st, a); break;
+    case PA_BF16: hipLaunchKernelGGL(combine_kernel<__bf16>, grid, dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

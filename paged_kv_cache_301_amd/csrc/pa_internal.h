@@ -40,4 +40,7 @@ hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st);
 // multiples of this.
 constexpr int kTileTokens = 32;
 
+// Partitions per (sequence, head): the partition index is grid dimension y.
+constexpr int kMaxPartitions = 65535;
+
 }  // namespace pa

@@ -180,11 +180,15 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile
 }
 
 template <typename T, typename OutT, int G, bool SCALAR_K, bool SCALAR_V>
-__global__ __launch_bounds__(64) void mfma_kernel(Args a) {
+__global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
+    // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
+    // (which the dispatcher deals round-robin to the 8 XCDs) take different
+    // (sequence, kv head) pairs of the same partition index, so the live
+    // partitions of ragged contexts spread evenly over the XCDs.
+    const int kvh = blockIdx.x % a.Hkv;
+    const int s = blockIdx.x / a.Hkv;
+    const int p = blockIdx.y;
     const int lane = threadIdx.x;
     const int i = lane & 15;
     const int g = lane >> 4;
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(64) void mfma_kernel(Args a) {
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    dim3 grid(a.max_parts, a.Hkv, a.S);
+    dim3 grid(a.Hkv * a.S, a.max_parts);
     if (a.B % 16 == 0)
         hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, true>), grid, dim3(64), 0, st, a);
     else if (a.B % 4 == 0)

@@ -127,9 +127,13 @@ __device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const ValuTile
 
 template <typename T, typename OutT, int G, bool SCALAR>
 __global__ __launch_bounds__(64) void valu_kernel(Args a) {
-    const int p = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
+    // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
+    // (which the dispatcher deals round-robin to the 8 XCDs) take different
+    // (sequence, kv head) pairs of the same partition index, so the live
+    // partitions of ragged contexts spread evenly over the XCDs.
+    const int kvh = blockIdx.x % a.Hkv;
+    const int s = blockIdx.x / a.Hkv;
+    const int p = blockIdx.y;
     const int lane = threadIdx.x;
     const int c = lane & 15;
     const int g = lane >> 4;
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    dim3 grid(a.max_parts, a.Hkv, a.S);
+    dim3 grid(a.Hkv * a.S, a.max_parts);
     if (a.B % 4 == 0)
         hipLaunchKernelGGL((valu_kernel<T, OutT, G, true>), grid, dim3(64), 0, st, a);
     else
