@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--block-size", type=int, default=None, help="override B (gqa_long sweeps 1/8/16/32)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--kv-reuse", choices=["auto", "on", "off"], default="auto",
+                    help="cached (on) or streamed (off) K/V loads; auto = on when the workload "
+                         "shares a prompt prefix across sequences")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -146,19 +149,21 @@ def main():
         ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
     out = torch.empty_like(w.query)
     stream = torch.cuda.current_stream(dev)
+    kv_reuse = {"on": True, "off": False}.get(args.kv_reuse, bool(w.spec.prefix_tokens))
     kw = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, workspace=ws,
-              stream=stream)
+              stream=stream, kv_reuse=kv_reuse)
+    args_ = (w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale, out)
+    run_parts = binding.prepare(*args_, stages=binding.STAGE_PARTITIONS, **kw)
+    run_combine = binding.prepare(*args_, stages=binding.STAGE_COMBINE, **kw)
 
     def step(evs=None):
         if evs is not None:
             evs[0].record(stream)
-        binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale,
-                       out, stages=binding.STAGE_PARTITIONS, **kw)
+        run_parts()
         if evs is not None:
             evs[1].record(stream)
         if plan["split"]:
-            binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                           w.scale, out, stages=binding.STAGE_COMBINE, **kw)
+            run_combine()
         if evs is not None:
             evs[2].record(stream)
 
@@ -210,6 +215,7 @@ def main():
                    "B": w.B, "tokens": int(w.lens.sum()), "kv_bytes": kv,
                    "unique_kv_bytes": w.unique_kv_bytes() if w.spec.prefix_tokens else kv,
                    "kernel": kname, "partition_tokens": plan["partition_tokens"],
+                   "kv_reuse": kv_reuse,
                    "split": bool(plan["split"])},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),

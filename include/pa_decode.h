@@ -91,6 +91,13 @@ typedef struct {
                              partition, a positive multiple of 32.  A value at
                              or above max_blocks * B gives a single-pass plan.   */
     int stages;           /* 0 means PA_STAGE_ALL                                */
+    int kv_reuse;         /* 0: K / V rows are streamed with the non-temporal
+                             load hint (each row is read once per call: best
+                             when sequences share few blocks).  1: ordinary
+                             cached loads, for pools where many sequences of
+                             the batch share blocks (a common prompt prefix),
+                             so repeated rows can hit in L2 / Infinity Cache.
+                             Results are identical either way.                  */
 } pa_config;
 
 /* The plan a call will execute (filled by pa_decode_plan). */

@@ -34,7 +34,7 @@ _TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA
 
 class PaConfig(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("partition_tokens", ctypes.c_int),
-                ("stages", ctypes.c_int)]
+                ("stages", ctypes.c_int), ("kv_reuse", ctypes.c_int)]
 
 
 class PaPlan(ctypes.Structure):
@@ -99,9 +99,9 @@ def _check(status: int):
         raise PaError(status, status_string(status))
 
 
-def _config(kernel="auto", partition_tokens=0, stages=0) -> PaConfig:
+def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False) -> PaConfig:
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    return PaConfig(k, int(partition_tokens), int(stages))
+    return PaConfig(k, int(partition_tokens), int(stages), int(bool(kv_reuse)))
 
 
 def _shape_args(query, key_cache, block_tables, out_dtype):
@@ -114,12 +114,12 @@ def _shape_args(query, key_cache, block_tables, out_dtype):
 
 
 def plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype=None, *, kernel="auto",
-         partition_tokens=0, stages=0) -> dict:
+         partition_tokens=0, stages=0, kv_reuse=False) -> dict:
     """Resolve the plan for a shape (host only; no GPU needed)."""
     dt = _TORCH_TO_PA.get(dtype, dtype)
     odt = dt if out_dtype is None else _TORCH_TO_PA.get(out_dtype, out_dtype)
     p = PaPlan()
-    cfg = _config(kernel, partition_tokens, stages)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
     _check(load().pa_decode_plan(S, Hq, Hkv, D, B, NB, max_blocks, dt, odt,
                                  ctypes.byref(cfg), ctypes.byref(p)))
     return p.as_dict()
@@ -128,7 +128,7 @@ def plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype=None, *, kernel="aut
 def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            out: Optional[torch.Tensor] = None, *, out_dtype: Optional[torch.dtype] = None,
-           kernel="auto", partition_tokens: int = 0, stages: int = 0,
+           kernel="auto", partition_tokens: int = 0, stages: int = 0, kv_reuse: bool = False,
            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Paged decode attention: out[S,Hq,D] from query[S,Hq,D], K/V pools
     [NB,Hkv,B,D], block_tables[S,max_blocks] int32 and seq_lens[S] int32.
@@ -158,7 +158,7 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     shape = _shape_args(query, key_cache, block_tables, out_dtype)
     if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
         raise ValueError("seq_lens / block_tables do not match the batch size")
-    cfg = _config(kernel, partition_tokens, stages)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
     ws_ptr, ws_bytes = None, 0
@@ -173,6 +173,43 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
                             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
                             out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr, ws_bytes, st))
     return out
+
+
+class PreparedCall:
+    """A decode call with every argument marshalled once, for tight loops
+    (benchmarks, graph-free serving loops): calling it only crosses the C ABI.
+
+    The tensors passed to ``prepare`` must stay alive and unmoved."""
+
+    def __init__(self, fn, args):
+        self._fn = fn
+        self._args = args
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def prepare(query, key_cache, value_cache, block_tables, seq_lens, scale, out, *,
+            kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, workspace=None,
+            stream=None) -> PreparedCall:
+    """Validate once (by running the same checks as ``decode`` on a plan) and
+    return a PreparedCall that launches the configured stage(s)."""
+    lib = load()
+    shape = _shape_args(query, key_cache, block_tables, out.dtype)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    p = PaPlan()
+    _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
+    if p.workspace_bytes and workspace is None:
+        raise ValueError("this plan needs a workspace")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(query.device)
+    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    args = (query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+            block_tables.data_ptr(), seq_lens.data_ptr(), ctypes.c_float(scale),
+            out.data_ptr(), *shape, ctypes.pointer(cfg), ws_ptr, ctypes.c_size_t(ws_bytes), st)
+    return PreparedCall(lib.pa_decode_ex, args)
 
 
 def decode_workload(w, out_dtype=None, **kw) -> torch.Tensor:

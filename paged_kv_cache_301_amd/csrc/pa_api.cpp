@@ -180,7 +180,7 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     if (plan.kernel != PA_KERNEL_GENERIC &&
         !(aligned16(query) && aligned16(key_cache) && aligned16(value_cache) && aligned16(out))) {
         if (cfg && cfg->kernel != PA_KERNEL_AUTO) return PA_ERR_UNSUPPORTED;
-        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0};
+        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0, 0};
         st = make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, &gen, &plan);
         if (st != PA_OK) return st;
     }
@@ -206,6 +206,7 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     a.part_tokens = plan.partition_tokens;
     a.max_parts = plan.max_partitions;
     a.split = plan.split;
+    a.stream_kv = (cfg && cfg->kv_reuse) ? 0 : 1;
     if (plan.split) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
             workspace_bytes < plan.workspace_bytes)

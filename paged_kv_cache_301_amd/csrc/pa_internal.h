@@ -27,6 +27,7 @@ struct Args {
     int part_tokens;          // tokens per context partition
     int max_parts;            // partitions per (s, head) in the grid
     int split;                // 1: write partials, 0: write final output
+    int stream_kv;            // 1: K / V loads carry the non-temporal hint
 };
 
 // Launchers return hipErrorInvalidValue when no instantiation covers the

@@ -75,7 +75,7 @@ struct MfmaTile {
 
 // SCALAR_K: the 16 rows of a K sub-tile share one block (B % 16 == 0).
 // SCALAR_V: the 4 rows of a V load share one block (B % 4 == 0).
-template <bool SCALAR_K, bool SCALAR_V>
+template <bool SCALAR_K, bool SCALAR_V, bool STREAM>
 struct MfmaCtx {
     const char *kbase;     // key_cache + kv head offset (bytes)
     const char *vbase;     // value_cache + kv head offset + 16 * i (bytes)
@@ -93,21 +93,41 @@ struct MfmaCtx {
             const int phys = phys_block<SCALAR_K>(tv, tbl, t);
             const char *row = kbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2) + 16 * g;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) tile.k[u][kk] = *reinterpret_cast<const uint4 *>(row + 64 * kk);
+            for (int kk = 0; kk < 4; ++kk) tile.k[u][kk] = load_kv16<STREAM>(row + 64 * kk);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int t = min(t0 + 4 * k + g, t_end - 1);
             const int phys = phys_block<SCALAR_V>(tv, tbl, t);
-            tile.v[k] = *reinterpret_cast<const uint4 *>(
-                vbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2));
+            tile.v[k] = load_kv16<STREAM>(vbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2));
         }
     }
 };
 
-// LDS image of one iteration's V: 32 token rows x 16 chunks of 16 bytes, the
-// chunk index XORed with 2 * ((row / 4) % 4).
-__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ (2 * ((row >> 2) & 3)); }
+// LDS image of one iteration's V: 32 token rows of 256 bytes (16 chunks of
+// 16 bytes).  Chunk c of row r sits at chunk position c ^ swz(r).
+//
+// The V^T operand is read with ds_read_b64_tr_b16.  Within each 16-lane
+// group, lane q addresses 8 bytes (4 consecutive elements) and receives, in
+// result slot r, element (q % 4) of the 4-vector addressed by lane 4r + q / 4.
+// Lane q of group g therefore addresses row 4g + q / 4 (the second read: 16
+// rows further), elements 16n + 4 (q % 4) .. +3, and receives
+// V[4g + r][16n + q] (second read: V[16 + 4g + r][16n + q]) for r = 0..3:
+// exactly the A-operand slots k = (g, r) and (g, 4 + r).
+//
+// swz(r) = 2 ((r / 2) % 8) spreads the 16 rows one read touches over 8 even
+// chunk offsets, so its 64 eight-byte accesses fill all 64 LDS banks twice
+// (the minimum for 512 bytes); the 16-byte row writes stay conflict free.
+__device__ __forceinline__ int swz(int row) { return 2 * ((row >> 1) & 7); }
+
+using i16x4 = short __attribute__((ext_vector_type(4)));
+using lds_i16x4 = __attribute__((address_space(3))) i16x4;
+using lds_char = __attribute__((address_space(3))) char;
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint4 *lds_base, int byte_off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)((lds_char *)lds_base + byte_off));
+}
 
 template <typename T, int G>
 struct MfmaState {
@@ -125,7 +145,7 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile
     using Vec = typename M::Vec;
     // V rows to LDS (row 4k + g, swizzled chunk)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) vlds[(4 * k + g) * 16 + swz_chunk(4 * k + g, i)] = tile.v[k];
+    for (int k = 0; k < 8; ++k) vlds[(4 * k + g) * 16 + (i ^ swz(4 * k + g))] = tile.v[k];
 
     // scores
     float x[8];
@@ -160,26 +180,21 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile
     split_probs<T>(p, phi, plo);
 
     __syncthreads();   // V rows visible to every lane
-    const u16 *vl = reinterpret_cast<const u16 *>(vlds);
+    const int row_a = 4 * g + (i >> 2);
+    const int sw = swz(row_a);
+    const int lane_off = row_a * 256 + ((i & 3) << 3);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-        // column 16n + i of rows 4g + j (j < 4) and 16 + 4g + j - 4; the swizzle
-        // term of all eight rows is 2g
-        const int col = ((((2 * n + (i >> 3)) ^ (2 * g)) * 16) >> 1) + (i & 7);
-        const int rbase = (4 * g) * 128;
-        Vec va;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int row_off = (j < 4 ? j : 16 + j - 4) * 128;
-            va[j] = bitcast<T>(vl[rbase + row_off + col]);
-        }
+        const int off = lane_off + (((2 * n) ^ sw) << 4);
+        struct { i16x4 a, b; } raw = {lds_read_tr16(vlds, off), lds_read_tr16(vlds, off + 16 * 256)};
+        const Vec va = bitcast<Vec>(raw);
         st.o[n] = M::mma(va, phi, st.o[n]);
         st.o[n] = M::mma(va, plo, st.o[n]);
     }
     __syncthreads();   // reads done before the next iteration overwrites LDS
 }
 
-template <typename T, typename OutT, int G, bool SCALAR_K, bool SCALAR_V>
+template <typename T, typename OutT, int G, bool SCALAR_K, bool SCALAR_V, bool STREAM>
 __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
     // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
@@ -220,7 +235,7 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     st.l = 0.f;
 
     if (L > 0) {
-        MfmaCtx<SCALAR_K, SCALAR_V> ctx;
+        MfmaCtx<SCALAR_K, SCALAR_V, STREAM> ctx;
         const size_t head_bytes = (size_t)a.B * kD * 2;
         ctx.kbase = static_cast<const char *>(a.key_cache) + kvh * head_bytes;
         ctx.vbase = static_cast<const char *>(a.value_cache) + kvh * head_bytes + 16 * i;
@@ -276,15 +291,21 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     }
 }
 
-template <typename T, typename OutT, int G>
-hipError_t launch_g(const Args &a, hipStream_t st) {
+template <typename T, typename OutT, int G, bool STREAM>
+void launch_gs(const Args &a, hipStream_t st) {
     dim3 grid(a.Hkv * a.S, a.max_parts);
     if (a.B % 16 == 0)
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, true>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, true, STREAM>), grid, dim3(64), 0, st, a);
     else if (a.B % 4 == 0)
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, true>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, true, STREAM>), grid, dim3(64), 0, st, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, false>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, false, STREAM>), grid, dim3(64), 0, st, a);
+}
+
+template <typename T, typename OutT, int G>
+hipError_t launch_g(const Args &a, hipStream_t st) {
+    if (a.stream_kv) launch_gs<T, OutT, G, true>(a, st);
+    else launch_gs<T, OutT, G, false>(a, st);
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ struct ValuTile {
     uint4 v[kLoads];
 };
 
-template <bool SCALAR>
+template <bool SCALAR, bool STREAM>
 struct ValuCtx {
     const char *kbase;     // key_cache + kv head offset + lane column (bytes)
     const char *vbase;
@@ -58,8 +58,8 @@ struct ValuCtx {
             const int t = min(t0 + 4 * k + g, t_end - 1);
             const int phys = phys_block<SCALAR>(tv, tbl, t);
             const size_t off = (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2);
-            tile.k[k] = *reinterpret_cast<const uint4 *>(kbase + off);
-            tile.v[k] = *reinterpret_cast<const uint4 *>(vbase + off);
+            tile.k[k] = load_kv16<STREAM>(kbase + off);
+            tile.v[k] = load_kv16<STREAM>(vbase + off);
         }
     }
 };
@@ -125,7 +125,7 @@ __device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const ValuTile
     }
 }
 
-template <typename T, typename OutT, int G, bool SCALAR>
+template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
 __global__ __launch_bounds__(64) void valu_kernel(Args a) {
     // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
     // (which the dispatcher deals round-robin to the 8 XCDs) take different
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
     }
 
     if (L > 0) {
-        ValuCtx<SCALAR> ctx;
+        ValuCtx<SCALAR, STREAM> ctx;
         const size_t head_bytes = (size_t)a.B * kD * 2;
         ctx.kbase = static_cast<const char *>(a.key_cache) + kvh * head_bytes + 16 * c;
         ctx.vbase = static_cast<const char *>(a.value_cache) + kvh * head_bytes + 16 * c;
@@ -232,10 +232,14 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
     dim3 grid(a.Hkv * a.S, a.max_parts);
-    if (a.B % 4 == 0)
-        hipLaunchKernelGGL((valu_kernel<T, OutT, G, true>), grid, dim3(64), 0, st, a);
-    else
-        hipLaunchKernelGGL((valu_kernel<T, OutT, G, false>), grid, dim3(64), 0, st, a);
+    const bool scalar = a.B % 4 == 0;
+    if (a.stream_kv) {
+        if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, true, true>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((valu_kernel<T, OutT, G, false, true>), grid, dim3(64), 0, st, a);
+    } else {
+        if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, true, false>), grid, dim3(64), 0, st, a);
+        else hipLaunchKernelGGL((valu_kernel<T, OutT, G, false, false>), grid, dim3(64), 0, st, a);
+    }
     return hipGetLastError();
 }
 

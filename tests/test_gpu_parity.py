@@ -253,3 +253,18 @@ def test_full_size_sampled(name, over):
     out2 = run(w)
     got2 = out2.reshape(w.S * w.Hq, w.D)[torch.as_tensor(rows, device=DEV)]
     check(got2, ref, w.dtype, name + "/native")
+
+
+@pytest.mark.parametrize("kernel,Hq,Hkv,B", [("valu", 8, 8, 16), ("valu", 8, 8, 1), ("mfma", 16, 2, 16),
+                                             ("mfma", 16, 4, 8)])
+def test_kv_reuse_hint_is_bit_identical(kernel, Hq, Hkv, B):
+    """Streamed and cached K/V loads differ only in cache policy."""
+    say(f"case: kv_reuse on/off {kernel} B={B}")
+    spec = workloads.WorkloadSpec("hint", S=4, Hq=Hq, Hkv=Hkv, D=128, B=B, dtype="bf16",
+                                  lens=("fixed", (7, 100, 513, 1000)), max_len=1024,
+                                  pool=("free", 0.3), seed=31)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    a = run(w, out_dtype=torch.float32, kernel=kernel, partition_tokens=256, kv_reuse=False)
+    b2 = run(w, out_dtype=torch.float32, kernel=kernel, partition_tokens=256, kv_reuse=True)
+    assert torch.equal(a, b2)
+    check(a, oracle_full(w), torch.bfloat16, kernel)
