@@ -13,19 +13,23 @@ namespace {
 
 using pa::Args;
 
-// Automatic partition size: kAutoPartitionMax tokens, halved (down to
-// kAutoPartitionMin) while the grid would hold fewer than kAutoMinItems
-// (sequence, kv head, partition) items -- small batches need shorter
-// partitions to occupy 256 CUs; large ones amortise the combine pass.
-constexpr int kAutoPartitionMax = 512;
-constexpr int kAutoPartitionMin = 64;
-constexpr long long kAutoMinItems = 8192;
+// Automatic partition size: at least kAutoPartitionMin tokens and at most
+// kAutoMaxParts partitions per context (long contexts: fewer, longer
+// partitions keep the combine pass and the partial results small), then
+// halved (down to kAutoPartitionFloor) while the grid would hold fewer than
+// kAutoMinItems (sequence, kv head, partition) items, so small batches still
+// occupy 256 CUs.  Contexts of at most kAutoSinglePass tokens run in one pass.
+constexpr long long kAutoPartitionMin = 512;
+constexpr long long kAutoMaxParts = 32;
+constexpr long long kAutoPartitionFloor = 64;
+constexpr long long kAutoMinItems = 4096;
 constexpr long long kAutoSinglePass = 256;
 
 long long auto_partition(int S, int Hkv, long long max_ctx) {
-    if (max_ctx <= kAutoSinglePass) return max_ctx;   // short contexts: one pass
-    long long part = kAutoPartitionMax;
-    while (part > kAutoPartitionMin &&
+    if (max_ctx <= kAutoSinglePass) return max_ctx;
+    long long part = kAutoPartitionMin;
+    while (part * kAutoMaxParts < max_ctx) part *= 2;
+    while (part > kAutoPartitionFloor &&
            (long long)S * Hkv * ((max_ctx + part - 1) / part) < kAutoMinItems)
         part /= 2;
     return part;
@@ -69,11 +73,10 @@ bool supports_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
            (G == 4 || G == 8 || G == 16);
 }
 
-// Largest partition whose block-table slice fits the LDS copy (kernels that
-// stage the table: VALU with B % 4 != 0, MFMA with B % 16 != 0).
+// Largest partition whose block-table slice fits the LDS copy (the tiled
+// kernels stage the table when B % 4 != 0).
 long long table_cap(int kernel, int B) {
-    const bool staged = (kernel == PA_KERNEL_VALU && B % 4 != 0) ||
-                        (kernel == PA_KERNEL_MFMA && B % 16 != 0);
+    const bool staged = (kernel == PA_KERNEL_VALU || kernel == PA_KERNEL_MFMA) && B % 4 != 0;
     return staged ? 1024LL * B : (long long)INT_MAX;
 }
 
@@ -207,6 +210,9 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     a.max_parts = plan.max_partitions;
     a.split = plan.split;
     a.stream_kv = (cfg && cfg->kv_reuse) ? 0 : 1;
+    // live-item grid when every work-group can decode its item from the
+    // lengths held in one wave's registers, and the 1-D grid fits
+    a.compact = (S <= 1024 && (long long)S * Hkv * plan.max_partitions * 64 < (1LL << 32)) ? 1 : 0;
     if (plan.split) {
         if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
             workspace_bytes < plan.workspace_bytes)

@@ -28,6 +28,7 @@ struct Args {
     int max_parts;            // partitions per (s, head) in the grid
     int split;                // 1: write partials, 0: write final output
     int stream_kv;            // 1: K / V loads carry the non-temporal hint
+    int compact;              // 1: 1-D grid decoded into live items (pa_sched.h)
 };
 
 // Launchers return hipErrorInvalidValue when no instantiation covers the

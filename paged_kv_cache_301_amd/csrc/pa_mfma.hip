@@ -9,20 +9,19 @@
 // columns.  One wave64 handles one (sequence, kv head, context partition); an
 // iteration covers 32 tokens (two 16-row score tiles, one 32-deep P.V step).
 //
-// Operand layouts (lane = 16 * g + i):
-//  * QK, A = K rows: lane reads token i of a 16-token sub-tile, elements
-//    8g + 32kk .. +7 of the row (one 16-byte load per kk).  B = Q^T: lane holds
-//    q[head i] at the same elements, loaded once.
+// K and V arrive as whole token rows (pa_tile.h: full 128-byte lines per load
+// instruction) and are staged through LDS, from where each operand is read in
+// the matrix core's lane layout (lane = 16 g + i):
+//  * QK, A = K rows: lane holds token i of a 16-token sub-tile, elements
+//    8g + 32kk .. +7 (16-byte chunk 4kk + g), read with ds_read_b128.
+//    B = Q^T: lane holds q[head i] at the same elements, loaded once.
 //  * The result lane holds S^T[4g + r][i], r = 0..3: scores of four tokens for
 //    head i.  The two sub-tiles give the lane tokens {4g+r} and {16+4g+r}.
 //  * PV, B = P^T: lane holds P[head i] at exactly those eight tokens, so the
 //    contraction index k = (g, j) maps to token 4g + j (j < 4) or
 //    16 + 4g + j - 4 (j >= 4) and no probability moves between lanes.
-//  * PV, A = V^T: lane holds V[token(g, j)][16n + i] for d-chunk n.  V arrives
-//    token-major, so it is staged through LDS: whole 1 KB rows are written
-//    with 16-byte stores (16-byte chunks XOR-swizzled by row so the column
-//    reads below are bank-conflict free) and read back one column element at
-//    a time.
+//  * PV, A = V^T: lane holds V[token(g, j)][16n + i] for d-chunk n, read with
+//    ds_read_b64_tr_b16 (see swz_v below).
 //  * The PV result lane holds O^T[16n + 4g + r][i]: four consecutive output
 //    elements of head i, and the softmax rescale factor of head i is lane-local.
 //
@@ -34,12 +33,14 @@
 #include "pa_internal.h"
 #include "pa_device.h"
 #include "pa_table.h"
+#include "pa_tile.h"
+#include "pa_sched.h"
 
 namespace pa {
 
 namespace {
 
-constexpr int kD = 128;
+constexpr int kD = kHeadDim;
 
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
@@ -68,57 +69,27 @@ __device__ __forceinline__ void split_probs(const float (&p)[8], Vec &hi, Vec &l
     }
 }
 
-struct MfmaTile {
-    uint4 k[2][4];   // [sub-tile][kk]
-    uint4 v[8];      // token 4k + g, chunk i
-};
-
-// SCALAR_K: the 16 rows of a K sub-tile share one block (B % 16 == 0).
-// SCALAR_V: the 4 rows of a V load share one block (B % 4 == 0).
-template <bool SCALAR_K, bool SCALAR_V, bool STREAM>
-struct MfmaCtx {
-    const char *kbase;     // key_cache + kv head offset (bytes)
-    const char *vbase;     // value_cache + kv head offset + 16 * i (bytes)
-    size_t block_bytes;
-    int bmask;
-    int t_end;
-    int g, i;
-    TableView tv;
-    const int32_t *tbl;
-
-    __device__ __forceinline__ void load(MfmaTile &tile, int t0) const {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = min(t0 + 16 * u + i, t_end - 1);
-            const int phys = phys_block<SCALAR_K>(tv, tbl, t);
-            const char *row = kbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2) + 16 * g;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) tile.k[u][kk] = load_kv16<STREAM>(row + 64 * kk);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int t = min(t0 + 4 * k + g, t_end - 1);
-            const int phys = phys_block<SCALAR_V>(tv, tbl, t);
-            tile.v[k] = load_kv16<STREAM>(vbase + (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2));
-        }
-    }
-};
-
-// LDS image of one iteration's V: 32 token rows of 256 bytes (16 chunks of
-// 16 bytes).  Chunk c of row r sits at chunk position c ^ swz(r).
+// LDS images of one iteration: 32 token rows of 256 bytes (16 chunks of 16
+// bytes) for K and for V; chunk c of row r is stored at c ^ swz(r).
 //
-// The V^T operand is read with ds_read_b64_tr_b16.  Within each 16-lane
-// group, lane q addresses 8 bytes (4 consecutive elements) and receives, in
-// result slot r, element (q % 4) of the 4-vector addressed by lane 4r + q / 4.
-// Lane q of group g therefore addresses row 4g + q / 4 (the second read: 16
-// rows further), elements 16n + 4 (q % 4) .. +3, and receives
-// V[4g + r][16n + q] (second read: V[16 + 4g + r][16n + q]) for r = 0..3:
-// exactly the A-operand slots k = (g, r) and (g, 4 + r).
+// K: swz_k(r) = r % 16.  A QK operand read (fixed kk) has the 16 lanes of a
+// group on 16 rows at one logical chunk, which the swizzle spreads over all 16
+// chunk positions, i.e. all 64 banks.
 //
-// swz(r) = 2 ((r / 2) % 8) spreads the 16 rows one read touches over 8 even
-// chunk offsets, so its 64 eight-byte accesses fill all 64 LDS banks twice
-// (the minimum for 512 bytes); the 16-byte row writes stay conflict free.
-__device__ __forceinline__ int swz(int row) { return 2 * ((row >> 1) & 7); }
+// V: read with ds_read_b64_tr_b16.  Within each 16-lane group, lane q
+// addresses 8 bytes (4 consecutive elements) and receives, in result slot r,
+// element (q % 4) of the 4-vector addressed by lane 4r + q / 4.  Lane q of
+// group g therefore addresses row 4g + q / 4 (the second read: 16 rows
+// further), elements 16n + 4 (q % 4) .. +3, and receives V[4g + r][16n + q]
+// (second read: V[16 + 4g + r][16n + q]) for r = 0..3: exactly the A-operand
+// slots k = (g, r) and (g, 4 + r).  swz_v(r) = 2 ((r / 2) % 8) spreads the 16
+// rows one such read touches over 8 even chunk offsets, so its 64 eight-byte
+// accesses fill all 64 banks twice (the minimum for 512 bytes).
+//
+// The 16-byte row writes of both images are conflict free (each row is a
+// permutation of its 16 chunks).
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return 2 * ((row >> 1) & 7); }
 
 using i16x4 = short __attribute__((ext_vector_type(4)));
 using lds_i16x4 = __attribute__((address_space(3))) i16x4;
@@ -137,23 +108,31 @@ struct MfmaState {
 };
 
 template <typename T, int G>
-__device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile &tile,
+__device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const KVTile &tile,
                                              const typename Mfma<T>::Vec (&qf)[4],
-                                             uint4 *vlds, int t0, int t_end, int g, int i,
-                                             float scale_log2) {
+                                             uint4 *klds, uint4 *vlds, int t0, int t_end,
+                                             int g, int i, float scale_log2) {
     using M = Mfma<T>;
     using Vec = typename M::Vec;
-    // V rows to LDS (row 4k + g, swizzled chunk)
+    // rows 4k + g, chunk i, to the swizzled LDS images
 #pragma unroll
-    for (int k = 0; k < 8; ++k) vlds[(4 * k + g) * 16 + (i ^ swz(4 * k + g))] = tile.v[k];
+    for (int k = 0; k < kTileLoads; ++k) {
+        const int row = 4 * k + g;
+        klds[row * 16 + (i ^ swz_k(row))] = tile.k[k];
+        vlds[row * 16 + (i ^ swz_v(row))] = tile.v[k];
+    }
+    __syncthreads();   // rows visible to every lane
 
-    // scores
+    // scores: A operand = chunk 4kk + g of row 16u + i (swizzle swz_k = i)
     float x[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = M::mma(bitcast<Vec>(tile.k[u][kk]), qf[kk], acc);
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint4 a = klds[(16 * u + i) * 16 + ((4 * kk + g) ^ i)];
+            acc = M::mma(bitcast<Vec>(a), qf[kk], acc);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             x[4 * u + r] = (t0 + 16 * u + 4 * g + r < t_end) ? acc[r] * scale_log2 : kNegInf;
@@ -179,14 +158,13 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile
     Vec phi, plo;
     split_probs<T>(p, phi, plo);
 
-    __syncthreads();   // V rows visible to every lane
     const int row_a = 4 * g + (i >> 2);
-    const int sw = swz(row_a);
-    const int lane_off = row_a * 256 + ((i & 3) << 3);
+    const int sw = swz_v(row_a);
+    const int lane_off = row_a * kRowBytes + ((i & 3) << 3);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
         const int off = lane_off + (((2 * n) ^ sw) << 4);
-        struct { i16x4 a, b; } raw = {lds_read_tr16(vlds, off), lds_read_tr16(vlds, off + 16 * 256)};
+        struct { i16x4 a, b; } raw = {lds_read_tr16(vlds, off), lds_read_tr16(vlds, off + 16 * kRowBytes)};
         const Vec va = bitcast<Vec>(raw);
         st.o[n] = M::mma(va, phi, st.o[n]);
         st.o[n] = M::mma(va, plo, st.o[n]);
@@ -194,16 +172,26 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const MfmaTile
     __syncthreads();   // reads done before the next iteration overwrites LDS
 }
 
-template <typename T, typename OutT, int G, bool SCALAR_K, bool SCALAR_V, bool STREAM>
+template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
 __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
-    // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
-    // (which the dispatcher deals round-robin to the 8 XCDs) take different
-    // (sequence, kv head) pairs of the same partition index, so the live
-    // partitions of ragged contexts spread evenly over the XCDs.
-    const int kvh = blockIdx.x % a.Hkv;
-    const int s = blockIdx.x / a.Hkv;
-    const int p = blockIdx.y;
+    int s, kvh, p;
+    if (a.compact) {
+        // 1-D grid over the live items, partition-major (see pa_sched.h)
+        const WorkItem w = decode_work_item(a.seq_lens, a.S, a.Hkv, a.part_tokens, a.max_parts,
+                                            blockIdx.x);
+        if (!w.valid) return;
+        s = w.s;
+        kvh = w.kvh;
+        p = w.p;
+    } else {
+        // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
+        // (dealt round-robin to the 8 XCDs) take different (sequence, kv head)
+        // pairs of one partition index, spreading ragged contexts over XCDs
+        kvh = blockIdx.x % a.Hkv;
+        s = blockIdx.x / a.Hkv;
+        p = blockIdx.y;
+    }
     const int lane = threadIdx.x;
     const int i = lane & 15;
     const int g = lane >> 4;
@@ -214,8 +202,9 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     const int t_end = min(L, t_begin + a.part_tokens);
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
+    __shared__ uint4 klds[32 * 16];
     __shared__ uint4 vlds[32 * 16];
-    __shared__ int32_t tbl[(SCALAR_K && SCALAR_V) ? 1 : kTableLds];
+    __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
 
     // Q^T fragments; columns past the group are zero
     Vec qf[4];
@@ -235,33 +224,40 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     st.l = 0.f;
 
     if (L > 0) {
-        MfmaCtx<SCALAR_K, SCALAR_V, STREAM> ctx;
-        const size_t head_bytes = (size_t)a.B * kD * 2;
-        ctx.kbase = static_cast<const char *>(a.key_cache) + kvh * head_bytes;
+        TileLoader<SCALAR, STREAM> ctx;
+        const size_t head_bytes = (size_t)a.B * kRowBytes;
+        ctx.kbase = static_cast<const char *>(a.key_cache) + kvh * head_bytes + 16 * i;
         ctx.vbase = static_cast<const char *>(a.value_cache) + kvh * head_bytes + 16 * i;
         ctx.block_bytes = (size_t)a.Hkv * head_bytes;
         ctx.bmask = a.B - 1;
         ctx.t_end = t_end;
         ctx.g = g;
-        ctx.i = i;
         ctx.tv.row = a.block_tables + (size_t)s * a.max_blocks;
         ctx.tv.lb = a.log2B;
         ctx.tv.j0 = t_begin >> a.log2B;
         ctx.tbl = tbl;
-        if constexpr (!(SCALAR_K && SCALAR_V)) {
+        if constexpr (!SCALAR) {
             stage_table(tbl, ctx.tv, t_begin, t_end, lane, 64);
             __syncthreads();
         }
 
         const int niter = (t_end - t_begin + 31) >> 5;
-        MfmaTile ta, tb;
+        KVTile ta, tb;
         ctx.load(ta, t_begin);
+        // The scheduling barriers keep each prefetch ahead of the wait for
+        // the tile computed next; without them the compiler sinks the loads
+        // below that wait and the wave never has two tiles in flight.
         for (int it = 0; it < niter; it += 2) {
             const int t0 = t_begin + 32 * it;
             ctx.load(tb, t0 + 32);
-            mfma_compute<T, G>(st, ta, qf, vlds, t0, t_end, g, i, a.scale_log2);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_compute<T, G>(st, ta, qf, klds, vlds, t0, t_end, g, i, a.scale_log2);
+            __builtin_amdgcn_sched_barrier(0);
             ctx.load(ta, t0 + 64);
-            if (it + 1 < niter) mfma_compute<T, G>(st, tb, qf, vlds, t0 + 32, t_end, g, i, a.scale_log2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 1 < niter)
+                mfma_compute<T, G>(st, tb, qf, klds, vlds, t0 + 32, t_end, g, i, a.scale_log2);
+            __builtin_amdgcn_sched_barrier(0);
         }
         st.l += shfl_xor(st.l, 16);
         st.l += shfl_xor(st.l, 32);
@@ -293,13 +289,12 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
 
 template <typename T, typename OutT, int G, bool STREAM>
 void launch_gs(const Args &a, hipStream_t st) {
-    dim3 grid(a.Hkv * a.S, a.max_parts);
-    if (a.B % 16 == 0)
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, true, STREAM>), grid, dim3(64), 0, st, a);
-    else if (a.B % 4 == 0)
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, true, STREAM>), grid, dim3(64), 0, st, a);
+    const dim3 grid = a.compact ? dim3((unsigned)((long long)a.Hkv * a.S * a.max_parts))
+                                : dim3(a.Hkv * a.S, a.max_parts);
+    if (a.B % 4 == 0)
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, STREAM>), grid, dim3(64), 0, st, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, false, STREAM>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, STREAM>), grid, dim3(64), 0, st, a);
 }
 
 template <typename T, typename OutT, int G>

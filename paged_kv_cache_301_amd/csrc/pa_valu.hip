@@ -28,41 +28,15 @@
 #include "pa_internal.h"
 #include "pa_device.h"
 #include "pa_table.h"
+#include "pa_tile.h"
+#include "pa_sched.h"
 
 namespace pa {
 
 namespace {
 
-constexpr int kD = 128;
-constexpr int kLoads = 8;   // load instructions per operand per iteration (32 tokens)
-
-struct ValuTile {
-    uint4 k[kLoads];
-    uint4 v[kLoads];
-};
-
-template <bool SCALAR, bool STREAM>
-struct ValuCtx {
-    const char *kbase;     // key_cache + kv head offset + lane column (bytes)
-    const char *vbase;
-    size_t block_bytes;    // bytes between consecutive physical blocks
-    int bmask;             // B - 1
-    int t_end;             // one past the partition's last token
-    int g;                 // token row within a load instruction (lane >> 4)
-    TableView tv;
-    const int32_t *tbl;
-
-    __device__ __forceinline__ void load(ValuTile &tile, int t0) const {
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) {
-            const int t = min(t0 + 4 * k + g, t_end - 1);
-            const int phys = phys_block<SCALAR>(tv, tbl, t);
-            const size_t off = (size_t)phys * block_bytes + (size_t)(t & bmask) * (kD * 2);
-            tile.k[k] = load_kv16<STREAM>(kbase + off);
-            tile.v[k] = load_kv16<STREAM>(vbase + off);
-        }
-    }
-};
+constexpr int kD = kHeadDim;
+constexpr int kLoads = kTileLoads;
 
 template <typename T, int G>
 struct ValuState {
@@ -72,7 +46,7 @@ struct ValuState {
 };
 
 template <typename T, int G>
-__device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const ValuTile &tile,
+__device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const KVTile &tile,
                                              const uint4 (&q)[G], int t0, int t_end, int g,
                                              float scale_log2) {
     float x[G][kLoads];
@@ -127,13 +101,23 @@ __device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const ValuTile
 
 template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
 __global__ __launch_bounds__(64) void valu_kernel(Args a) {
-    // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
-    // (which the dispatcher deals round-robin to the 8 XCDs) take different
-    // (sequence, kv head) pairs of the same partition index, so the live
-    // partitions of ragged contexts spread evenly over the XCDs.
-    const int kvh = blockIdx.x % a.Hkv;
-    const int s = blockIdx.x / a.Hkv;
-    const int p = blockIdx.y;
+    int s, kvh, p;
+    if (a.compact) {
+        // 1-D grid over the live items, partition-major (see pa_sched.h)
+        const WorkItem w = decode_work_item(a.seq_lens, a.S, a.Hkv, a.part_tokens, a.max_parts,
+                                            blockIdx.x);
+        if (!w.valid) return;
+        s = w.s;
+        kvh = w.kvh;
+        p = w.p;
+    } else {
+        // x = (sequence, kv head) pairs, y = partition: consecutive work-groups
+        // (dealt round-robin to the 8 XCDs) take different (sequence, kv head)
+        // pairs of one partition index, spreading ragged contexts over XCDs
+        kvh = blockIdx.x % a.Hkv;
+        s = blockIdx.x / a.Hkv;
+        p = blockIdx.y;
+    }
     const int lane = threadIdx.x;
     const int c = lane & 15;
     const int g = lane >> 4;
@@ -162,7 +146,7 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
     }
 
     if (L > 0) {
-        ValuCtx<SCALAR, STREAM> ctx;
+        TileLoader<SCALAR, STREAM> ctx;
         const size_t head_bytes = (size_t)a.B * kD * 2;
         ctx.kbase = static_cast<const char *>(a.key_cache) + kvh * head_bytes + 16 * c;
         ctx.vbase = static_cast<const char *>(a.value_cache) + kvh * head_bytes + 16 * c;
@@ -180,14 +164,21 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         }
 
         const int niter = (t_end - t_begin + 31) >> 5;
-        ValuTile ta, tb;
+        KVTile ta, tb;
         ctx.load(ta, t_begin);
+        // The scheduling barriers keep each prefetch ahead of the wait for
+        // the tile computed next; without them the compiler sinks the loads
+        // below that wait and the wave never has two tiles in flight.
         for (int it = 0; it < niter; it += 2) {
             const int t0 = t_begin + 32 * it;
             ctx.load(tb, t0 + 32);
+            __builtin_amdgcn_sched_barrier(0);
             valu_compute<T, G>(st, ta, q, t0, t_end, g, a.scale_log2);
+            __builtin_amdgcn_sched_barrier(0);
             ctx.load(ta, t0 + 64);
+            __builtin_amdgcn_sched_barrier(0);
             if (it + 1 < niter) valu_compute<T, G>(st, tb, q, t0 + 32, t_end, g, a.scale_log2);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // merge the four row groups (lanes c, c+16, c+32, c+48 hold the same columns)
@@ -231,7 +222,8 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    dim3 grid(a.Hkv * a.S, a.max_parts);
+    const dim3 grid = a.compact ? dim3((unsigned)((long long)a.Hkv * a.S * a.max_parts))
+                                : dim3(a.Hkv * a.S, a.max_parts);
     const bool scalar = a.B % 4 == 0;
     if (a.stream_kv) {
         if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, true, true>), grid, dim3(64), 0, st, a);

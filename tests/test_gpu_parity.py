@@ -268,3 +268,17 @@ def test_kv_reuse_hint_is_bit_identical(kernel, Hq, Hkv, B):
     b2 = run(w, out_dtype=torch.float32, kernel=kernel, partition_tokens=256, kv_reuse=True)
     assert torch.equal(a, b2)
     check(a, oracle_full(w), torch.bfloat16, kernel)
+
+
+@pytest.mark.parametrize("kernel,Hq,Hkv,S", [("valu", 4, 4, 700), ("mfma", 16, 2, 700),
+                                             ("valu", 2, 2, 1100), ("mfma", 8, 2, 1100)])
+def test_many_sequences(kernel, Hq, Hkv, S):
+    """Batches beyond one wave's worth of lengths (live-item decode over
+    several register chunks) and beyond 1024 sequences (rectangular grid)."""
+    say(f"case: many sequences {kernel} S={S}")
+    spec = workloads.WorkloadSpec("many", S=S, Hq=Hq, Hkv=Hkv, D=128, B=16, dtype="bf16",
+                                  lens=("uniform", 0, 200), max_len=200, pool=("free", 0.2),
+                                  seed=S + Hq)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    out = run(w, out_dtype=torch.float32, kernel=kernel, partition_tokens=64)
+    check(out, oracle_full(w), torch.bfloat16, f"{kernel}/S{S}")
