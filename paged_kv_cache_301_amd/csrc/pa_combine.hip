@@ -11,9 +11,9 @@
 // partition kernel and are skipped here.
 //
 // One 256-thread work-group per (sequence, head): thread t owns output
-// columns 4 (t % 32) .. +3 and partitions t / 32, t / 32 + 8, ..., so every
-// partial row is read with full-width 16-byte loads and all partitions are in
-// flight at once; the eight partial sums meet in LDS.
+// columns 4 (t % 32) .. +3 and partitions t / 32, t / 32 + 8, ..., merged
+// online, so every partial row is read with full-width 16-byte loads and all
+// partitions are in flight at once; the eight group states meet in LDS.
 #include "pa_internal.h"
 #include "pa_device.h"
 
@@ -40,52 +40,58 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a) {
     const float *pl = a.part_l + row * a.max_parts;
     const float4 *po = reinterpret_cast<const float4 *>(a.part_o + row * a.max_parts * kD);
 
-    __shared__ float red[kThreads / 64];
     __shared__ float4 acc_s[kGroups][kCols];
+    __shared__ float m_s[kGroups];
     __shared__ float z_s[kGroups];
 
-    // M = max over partitions
-    float M = kNegInf;
-    for (int p = t; p < np; p += kThreads) M = fmaxf(M, pm[p]);
-    M = wave_max(M);
-    if ((t & 63) == 0) red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
+    // Each group of 32 threads merges partitions grp, grp + 8, ... online
+    // (running max), so no pass over the maxima precedes the loads.
     const int c = t % kCols;
     const int grp = t / kCols;
+    float m = kNegInf, z = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float z = 0.f;
     for (int p = grp; p < np; p += kGroups) {
-        const float w = fast_exp2(pm[p] - M);
+        const float mp = pm[p];
+        const float lp = pl[p];
         const float4 o = po[(size_t)p * kCols + c];
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
-        z = fmaf(w, pl[p], z);
+        const float mn = fmaxf(m, mp);          // finite: every partition holds a token
+        const float wa = fast_exp2(m - mn);     // 0 on the first partition
+        const float wb = fast_exp2(mp - mn);
+        z = z * wa + lp * wb;
+        acc.x = acc.x * wa + o.x * wb;
+        acc.y = acc.y * wa + o.y * wb;
+        acc.z = acc.z * wa + o.z * wb;
+        acc.w = acc.w * wa + o.w * wb;
+        m = mn;
     }
     acc_s[grp][c] = acc;
-    if (c == 0) z_s[grp] = z;
+    if (c == 0) {
+        m_s[grp] = m;
+        z_s[grp] = z;
+    }
     __syncthreads();
     if (grp != 0) return;
+    float M = kNegInf;
 #pragma unroll
-    for (int g = 1; g < kGroups; ++g) {
-        const float4 o = acc_s[g][c];
-        acc.x += o.x;
-        acc.y += o.y;
-        acc.z += o.z;
-        acc.w += o.w;
-    }
+    for (int k = 0; k < kGroups; ++k) M = fmaxf(M, m_s[k]);
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
     float Z = 0.f;
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) Z += z_s[g];
+    for (int k = 0; k < kGroups; ++k) {
+        const float w = fast_exp2(m_s[k] - M);  // groups without partitions: m = -inf, w = 0
+        const float4 o = acc_s[k][c];
+        r.x += w * o.x;
+        r.y += w * o.y;
+        r.z += w * o.z;
+        r.w += w * o.w;
+        Z += w * z_s[k];
+    }
     const float inv = 1.f / Z;
     const size_t base = row * kD + 4 * c;
-    store_elem<OutT>(a.out, base + 0, acc.x * inv);
-    store_elem<OutT>(a.out, base + 1, acc.y * inv);
-    store_elem<OutT>(a.out, base + 2, acc.z * inv);
-    store_elem<OutT>(a.out, base + 3, acc.w * inv);
+    store_elem<OutT>(a.out, base + 0, r.x * inv);
+    store_elem<OutT>(a.out, base + 1, r.y * inv);
+    store_elem<OutT>(a.out, base + 2, r.z * inv);
+    store_elem<OutT>(a.out, base + 3, r.w * inv);
 }
 
 }  // namespace
