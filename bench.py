@@ -46,6 +46,11 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the kernel-source hash used to match counter records, then exit")
+    ap.add_argument("--op", choices=["decode", "write_kv", "append_kv"], default="decode",
+                    help="decode (default): the attention step; write_kv: store a prompt chunk's "
+                         "K/V through a slot mapping; append_kv: store one new token per sequence")
+    ap.add_argument("--tokens", type=int, default=16384,
+                    help="write_kv: tokens in the chunk")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -112,6 +117,107 @@ def cpu_baseline(w, target_s):
             "seconds": round(dt, 2)}
 
 
+def write_slots(w, T, seed=11):
+    """Slot mapping of a T-token prompt chunk: the tokens fill whole blocks in
+    order, the blocks drawn at random (without repeats) from the pool."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    nblk = (T + w.B - 1) // w.B
+    if nblk > w.NB:
+        raise SystemExit(f"bench.py: {T} tokens need {nblk} blocks, the pool has {w.NB}")
+    blocks = rng.choice(w.NB, size=nblk, replace=False)
+    t = np.arange(T)
+    return (blocks[t // w.B] * w.B + t % w.B).astype(np.int32)
+
+
+def bench_write(args, w, dev):
+    """K/V write step: read the new rows, write them into their slots."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_301_amd import binding
+    g = torch.Generator(device=dev).manual_seed(12)
+    stream = torch.cuda.current_stream(dev)
+    if args.op == "write_kv":
+        T = args.tokens
+        slots = torch.from_numpy(write_slots(w, T)).to(dev)
+        key = torch.randn((T, w.Hkv, w.D), generator=g, device=dev).to(w.dtype)
+        value = torch.randn((T, w.Hkv, w.D), generator=g, device=dev).to(w.dtype)
+
+        def step():
+            binding.write_kv(key, value, slots, w.key_cache, w.value_cache, stream=stream)
+        meta_bytes = 4 * T
+    else:
+        T = w.S
+        key = torch.randn((T, w.Hkv, w.D), generator=g, device=dev).to(w.dtype)
+        value = torch.randn((T, w.Hkv, w.D), generator=g, device=dev).to(w.dtype)
+
+        def step():
+            binding.append_kv(key, value, w.block_tables, w.seq_lens, w.key_cache,
+                              w.value_cache, stream=stream)
+        meta_bytes = 8 * T       # length + one table entry per sequence
+    row_bytes = T * w.Hkv * w.D * w.esz * 2          # K and V rows
+    alg_bytes = 2 * row_bytes + meta_bytes           # read once, write once
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    step_ms = wall * 1e3 / args.steps
+    gbs = alg_bytes / (step_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+    print(f"[bench] {args.op}: T={T} rows {row_bytes / 1e6:.2f} MB, kernel {k_ms * 1e3:.2f} us, "
+          f"step {step_ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+    res = {
+        "metric": f"Paged KV {args.op.replace('_kv', '')}: K/V bytes moved per second (read + write)",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": f"{args.op}_{args.workload}", "tokens": T, "Hkv": w.Hkv,
+                   "D": w.D, "B": w.B, "NB": w.NB, "bytes": alg_bytes},
+        "kernel_us": round(k_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_kv_write", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        # host copy of the same rows; the pool holds just the blocks the
+        # write touches (renumbered in first-touch order), so the sample
+        # measures the row copies, not a copy of the whole pool
+        sm = (write_slots(w, T) if args.op == "write_kv" else
+              np.array([int(w.tables_host[s, (L - 1) // w.B]) * w.B + (L - 1) % w.B
+                        for s, L in enumerate(w.lens)], dtype=np.int64))
+        blk, off = sm // w.B, sm % w.B
+        _, ren = np.unique(blk, return_inverse=True)
+        sm_h = torch.from_numpy((ren * w.B + off).astype(np.int32))
+        nb = int(ren.max()) + 1
+        hk, hv = key.cpu(), value.cpu()
+        hkc = torch.zeros((nb, w.Hkv, w.B, w.D), dtype=w.dtype)
+        hvc = torch.zeros_like(hkc)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.write_kv(hk, hv, sm_h, hkc, hvc, inplace=True)
+            reps += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(alg_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"whole write ({T} tokens) into a host pool of the "
+                                         f"{nb} blocks it touches, {reps} pass(es)",
+                               "seconds": round(dt, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.print_source_sha:
@@ -142,6 +248,10 @@ def main():
           f"NB={w.NB} max_blocks={w.max_blocks} tokens={int(w.lens.sum())} "
           f"kv={w.kv_bytes() / 1e9:.3f} GB (generated in {time.perf_counter() - t_gen:.1f}s)",
           file=sys.stderr, flush=True)
+
+    if args.op != "decode":
+        bench_write(args, w, dev)
+        return
 
     plan = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype,
                         kernel=args.kernel, partition_tokens=args.partition_tokens)

@@ -168,6 +168,42 @@ pa_status pa_decode_ex(const void *query, const void *key_cache,
                        const pa_config *cfg, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/*
+ * pa_write_kv -- store new tokens' keys and values into their cache slots
+ * (page "PagedAttention by hand", section "Setup", Step 1, and the end of
+ * "Forward pass": a token's key and value are written into its slot of the
+ * sequence's physical block before attention runs).
+ *
+ *   key, value     [T][Hkv][D]      dtype, device
+ *   slot_mapping   [T]              int32, device: block * B + offset; a
+ *                                   negative value skips the token
+ *   key_cache, value_cache [NB][Hkv][B][D], device, updated in place
+ *
+ * Bits are copied unchanged.  Slots at or past NB * B are skipped.  Two tokens
+ * with the same slot race (one of them wins).  Asynchronous on `stream`.
+ * Errors: PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (dtype), PA_ERR_NULL, PA_ERR_HIP.
+ */
+pa_status pa_write_kv(const void *key, const void *value, const int32_t *slot_mapping,
+                      void *key_cache, void *value_cache, int T, int Hkv, int D, int B,
+                      int NB, pa_dtype dtype, void *stream);
+
+/*
+ * pa_append_kv -- the decode-step form of pa_write_kv: sequence s's new token
+ * is the last of its seq_lens[s] tokens (the lengths include it), so its rows
+ * go to block block_tables[s][(L - 1) / B], offset (L - 1) % B.
+ *
+ *   key, value     [S][Hkv][D]      dtype, device
+ *   block_tables   [S][max_blocks]  int32, device
+ *   seq_lens       [S]              int32, device
+ *
+ * Sequences with L <= 0, a table position past max_blocks, or a table entry
+ * outside [0, NB) are skipped.  Asynchronous on `stream`.
+ */
+pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_tables,
+                       const int32_t *seq_lens, void *key_cache, void *value_cache,
+                       int S, int Hkv, int D, int B, int NB, int max_blocks,
+                       pa_dtype dtype, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *pa_status_string(pa_status status);
 

@@ -57,6 +57,8 @@ def _load():
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_write_kv.restype = ctypes.c_longlong
+        lib.oracle_write_kv.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _lib = lib
@@ -84,6 +86,35 @@ def _dtype_code(t) -> int:
 def _host(t):
     """A contiguous CPU tensor (copies device tensors to the host)."""
     return t.detach().to("cpu").contiguous()
+
+
+def write_kv(key, value, slot_mapping, key_cache, value_cache, inplace=False):
+    """Store new tokens' K / V rows into their cache slots (copies of the host
+    caches are returned and the inputs are not modified, unless ``inplace``:
+    then the caches must be contiguous CPU tensors and are written directly).
+
+    key, value [T,Hkv,D]; slot_mapping [T] int32 (block * B + offset, negative
+    to skip); key_cache / value_cache [NB,Hkv,B,D].  Returns
+    (new_key_cache, new_value_cache, tokens_written).
+    """
+    import torch
+    k, v = _host(key), _host(value)
+    sm = _host(slot_mapping).to(torch.int32)
+    if inplace:
+        kc, vc = key_cache, value_cache
+        if kc.device.type != "cpu" or not (kc.is_contiguous() and vc.is_contiguous()):
+            raise ValueError("inplace needs contiguous host caches")
+    else:
+        kc, vc = _host(key_cache).clone(), _host(value_cache).clone()
+    T, Hkv, D = k.shape
+    NB, Hkv2, B, D2 = kc.shape
+    if (Hkv2, D2) != (Hkv, D) or v.shape != k.shape or vc.shape != kc.shape:
+        raise ValueError("shapes do not match")
+    if not (k.dtype == v.dtype == kc.dtype == vc.dtype):
+        raise TypeError("one element type expected")
+    n = _load().oracle_write_kv(k.data_ptr(), v.data_ptr(), sm.data_ptr(), kc.data_ptr(),
+                                vc.data_ptr(), T, Hkv, D, B, NB, k.element_size())
+    return kc, vc, int(n)
 
 
 def decode(query, key_cache, value_cache, block_tables, seq_lens, scale: float,

@@ -205,6 +205,42 @@ int oracle_decode(const void *query, const void *key_cache,
     return status;
 }
 
+/*
+ * oracle_write_kv -- store new tokens' keys and values into their cache slots.
+ *
+ * Page "PagedAttention by hand", section "Setup" (Step 1) and the end of
+ * "Forward pass" (Step 4): the current token's key and value are written into
+ * its slot of the sequence's physical block before attention runs.
+ *
+ *   key, value    [T][Hkv][D]        element size esz bytes
+ *   slot_mapping  [T]                physical slot = block * B + offset, or
+ *                                    negative to skip the token
+ *   key_cache, value_cache [NB][Hkv][B][D]
+ *
+ * Pure data movement: element bytes are copied unchanged.  Slots at or past
+ * NB * B are skipped (returned count excludes them).  Returns the number of
+ * tokens written.
+ */
+long long oracle_write_kv(const void *key, const void *value, const int32_t *slot_mapping,
+                          void *key_cache, void *value_cache, int T, int Hkv, int D, int B,
+                          int NB, int esz)
+{
+    long long written = 0;
+    for (int t = 0; t < T; ++t) {
+        long long slot = slot_mapping[t];
+        if (slot < 0 || slot >= (long long)NB * B) continue;
+        long long block = slot / B, offset = slot % B;
+        for (int h = 0; h < Hkv; ++h) {
+            size_t src = ((size_t)t * Hkv + h) * (size_t)D * esz;
+            size_t dst = (((size_t)block * Hkv + h) * B + offset) * (size_t)D * esz;
+            memcpy((char *)key_cache + dst, (const char *)key + src, (size_t)D * esz);
+            memcpy((char *)value_cache + dst, (const char *)value + src, (size_t)D * esz);
+        }
+        ++written;
+    }
+    return written;
+}
+
 /* Number of threads an OpenMP parallel region would use (for reporting). */
 int oracle_num_threads(void)
 {

@@ -78,6 +78,10 @@ def load():
     lib.pa_decode_ex.restype = _INT
     lib.pa_decode_ex.argtypes = tensors + _SHAPE + [ctypes.POINTER(PaConfig), _PTR,
                                                     ctypes.c_size_t, _PTR]
+    lib.pa_write_kv.restype = _INT
+    lib.pa_write_kv.argtypes = [_PTR] * 5 + [_INT] * 6 + [_PTR]
+    lib.pa_append_kv.restype = _INT
+    lib.pa_append_kv.argtypes = [_PTR] * 6 + [_INT] * 7 + [_PTR]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [_INT]
     _lib = lib
@@ -173,6 +177,56 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
                             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
                             out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr, ws_bytes, st))
     return out
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check_kv_pair(key, value, key_cache, value_cache):
+    for name, t in (("key", key), ("value", value), ("key_cache", key_cache),
+                    ("value_cache", value_cache)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if not (key.dtype == value.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("key, value and the caches must share one dtype")
+    if key.shape != value.shape or key_cache.shape != value_cache.shape:
+        raise ValueError("key/value or cache shapes differ")
+    if key.dim() != 3 or key_cache.dim() != 4 or key.shape[1:] != (key_cache.shape[1], key_cache.shape[3]):
+        raise ValueError("key must be [T,Hkv,D] and the caches [NB,Hkv,B,D]")
+
+
+def write_kv(key, value, slot_mapping, key_cache, value_cache, stream=None):
+    """Store key/value [T,Hkv,D] into their cache slots (slot_mapping [T] int32:
+    block * B + offset, negative to skip).  In place on the caches."""
+    lib = load()
+    _check_kv_pair(key, value, key_cache, value_cache)
+    if slot_mapping.dtype != torch.int32 or slot_mapping.shape != (key.shape[0],) or not slot_mapping.is_cuda:
+        raise ValueError("slot_mapping must be a GPU int32 tensor [T]")
+    T, Hkv, D = key.shape
+    NB, _, B, _ = key_cache.shape
+    _check(lib.pa_write_kv(key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(),
+                           key_cache.data_ptr(), value_cache.data_ptr(), T, Hkv, D, B, NB,
+                           _TORCH_TO_PA[key.dtype], _stream_handle(stream, key.device)))
+
+
+def append_kv(key, value, block_tables, seq_lens, key_cache, value_cache, stream=None):
+    """Decode-step write: sequence s's new token (the last of its seq_lens[s]
+    tokens) from key/value [S,Hkv,D] into its slot.  In place on the caches."""
+    lib = load()
+    _check_kv_pair(key, value, key_cache, value_cache)
+    S, Hkv, D = key.shape
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables / seq_lens do not match the batch")
+    NB, _, B, _ = key_cache.shape
+    _check(lib.pa_append_kv(key.data_ptr(), value.data_ptr(), block_tables.data_ptr(),
+                            seq_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                            S, Hkv, D, B, NB, block_tables.shape[1], _TORCH_TO_PA[key.dtype],
+                            _stream_handle(stream, key.device)))
 
 
 class PreparedCall:

@@ -252,6 +252,37 @@ pa_status pa_decode(const void *query, const void *key_cache, const void *value_
                         workspace_bytes, stream);
 }
 
+static int dtype_size(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+
+pa_status pa_write_kv(const void *key, const void *value, const int32_t *slot_mapping,
+                      void *key_cache, void *value_cache, int T, int Hkv, int D, int B, int NB,
+                      pa_dtype dtype, void *stream) {
+    if (T < 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0) return PA_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+    if (T == 0) return PA_OK;
+    if (!key || !value || !slot_mapping || !key_cache || !value_cache) return PA_ERR_NULL;
+    const hipError_t err = pa::launch_kv_write(key, value, slot_mapping, nullptr, nullptr,
+                                               key_cache, value_cache, T, Hkv, D, B, NB, 0,
+                                               dtype_size(dtype), static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_tables,
+                       const int32_t *seq_lens, void *key_cache, void *value_cache, int S,
+                       int Hkv, int D, int B, int NB, int max_blocks, pa_dtype dtype,
+                       void *stream) {
+    if (S < 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || max_blocks < 0) return PA_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+    if (S == 0) return PA_OK;
+    if (!key || !value || !block_tables || !seq_lens || !key_cache || !value_cache)
+        return PA_ERR_NULL;
+    const hipError_t err = pa::launch_kv_write(key, value, nullptr, block_tables, seq_lens,
+                                               key_cache, value_cache, S, Hkv, D, B, NB,
+                                               max_blocks, dtype_size(dtype),
+                                               static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 const char *pa_status_string(pa_status status) {
     switch (status) {
     case PA_OK: return "PA_OK";

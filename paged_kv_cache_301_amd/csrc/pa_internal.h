@@ -37,6 +37,10 @@ hipError_t launch_generic(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t 
 hipError_t launch_valu(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
 hipError_t launch_mfma(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
 hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st);
+hipError_t launch_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
+                           const int32_t *block_tables, const int32_t *seq_lens,
+                           void *key_cache, void *value_cache, int T, int Hkv, int D, int B,
+                           int NB, int max_blocks, int esz, hipStream_t st);
 
 // Tokens one loop iteration of the tiled kernels covers; partitions are
 // multiples of this.

@@ -109,3 +109,15 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         b.decode(q, kc, kc, torch.zeros(1, 2, dtype=torch.int32),
                  torch.ones(1, dtype=torch.int32), 1.0)
+
+
+def test_kv_write_validation(lib):
+    fake = 1 << 20
+    assert lib.pa_write_kv(fake, fake, fake, fake, fake, -1, 2, 8, 4, 4, F16, None) == b.PA_ERR_SHAPE
+    assert lib.pa_write_kv(fake, fake, fake, fake, fake, 3, 0, 8, 4, 4, F16, None) == b.PA_ERR_SHAPE
+    assert lib.pa_write_kv(fake, fake, fake, fake, fake, 3, 2, 8, 4, 4, 9, None) == b.PA_ERR_UNSUPPORTED
+    assert lib.pa_write_kv(fake, None, fake, fake, fake, 3, 2, 8, 4, 4, F16, None) == b.PA_ERR_NULL
+    assert lib.pa_write_kv(None, None, None, None, None, 0, 2, 8, 4, 4, F16, None) == b.PA_OK
+    assert lib.pa_append_kv(fake, fake, fake, fake, fake, fake, 2, 2, 8, 4, 4, -1, F16, None) == b.PA_ERR_SHAPE
+    assert lib.pa_append_kv(fake, fake, None, fake, fake, fake, 2, 2, 8, 4, 4, 3, F16, None) == b.PA_ERR_NULL
+    assert lib.pa_append_kv(None, None, None, None, None, None, 0, 2, 8, 4, 4, 3, F16, None) == b.PA_OK
