@@ -46,9 +46,12 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the kernel-source hash used to match counter records, then exit")
-    ap.add_argument("--op", choices=["decode", "write_kv", "append_kv"], default="decode",
+    ap.add_argument("--op", choices=["decode", "write_kv", "append_kv", "copy_blocks"],
+                    default="decode",
                     help="decode (default): the attention step; write_kv: store a prompt chunk's "
-                         "K/V through a slot mapping; append_kv: store one new token per sequence")
+                         "K/V through a slot mapping; append_kv: store one new token per sequence; "
+                         "copy_blocks: copy-on-write copies of --pairs whole blocks")
+    ap.add_argument("--pairs", type=int, default=1024, help="copy_blocks: blocks copied per step")
     ap.add_argument("--tokens", type=int, default=16384,
                     help="write_kv: tokens in the chunk")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -138,7 +141,19 @@ def bench_write(args, w, dev):
     from paged_kv_cache_301_amd import binding
     g = torch.Generator(device=dev).manual_seed(12)
     stream = torch.cuda.current_stream(dev)
-    if args.op == "write_kv":
+    if args.op == "copy_blocks":
+        rng = np.random.default_rng(13)
+        ids = rng.choice(w.NB, size=2 * args.pairs, replace=False)
+        pairs_h = torch.from_numpy(ids.reshape(2, -1).T.copy().astype(np.int32))
+        pairs = pairs_h.to(dev)
+        T = args.pairs
+
+        def step():
+            binding.copy_blocks(w.key_cache, w.value_cache, pairs, stream=stream)
+        block_bytes = w.Hkv * w.B * w.D * w.esz
+        row_bytes = T * block_bytes * 2                  # K and V blocks
+        meta_bytes = 8 * T
+    elif args.op == "write_kv":
         T = args.tokens
         slots = torch.from_numpy(write_slots(w, T)).to(dev)
         key = torch.randn((T, w.Hkv, w.D), generator=g, device=dev).to(w.dtype)
@@ -156,7 +171,8 @@ def bench_write(args, w, dev):
             binding.append_kv(key, value, w.block_tables, w.seq_lens, w.key_cache,
                               w.value_cache, stream=stream)
         meta_bytes = 8 * T       # length + one table entry per sequence
-    row_bytes = T * w.Hkv * w.D * w.esz * 2          # K and V rows
+    if args.op != "copy_blocks":
+        row_bytes = T * w.Hkv * w.D * w.esz * 2      # K and V rows
     alg_bytes = 2 * row_bytes + meta_bytes           # read once, write once
     for _ in range(args.warmup):
         step()
@@ -174,6 +190,7 @@ def bench_write(args, w, dev):
     step_ms = wall * 1e3 / args.steps
     gbs = alg_bytes / (step_ms * 1e-3) / 1e9
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+    kernel = "pa_copy_blocks" if args.op == "copy_blocks" else "pa_kv_write"
     print(f"[bench] {args.op}: T={T} rows {row_bytes / 1e6:.2f} MB, kernel {k_ms * 1e3:.2f} us, "
           f"step {step_ms * 1e3:.2f} us", file=sys.stderr, flush=True)
     res = {
@@ -183,14 +200,32 @@ def bench_write(args, w, dev):
         "scaling": "weak", "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype],
         "data": "synthetic",
-        "config": {"workload": f"{args.op}_{args.workload}", "tokens": T, "Hkv": w.Hkv,
+        "config": {"workload": f"{args.op}_{args.workload}",
+                   ("pairs" if args.op == "copy_blocks" else "tokens"): T, "Hkv": w.Hkv,
                    "D": w.D, "B": w.B, "NB": w.NB, "bytes": alg_bytes},
         "kernel_us": round(k_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "pa_kv_write", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.op == "copy_blocks":
+        from oracle.block_manager import copy_blocks as oracle_copy
+        # host pool of just the blocks the copies touch (renumbered)
+        ids_h = pairs_h.flatten().numpy()
+        small = torch.arange(len(ids_h), dtype=torch.int32).reshape(-1, 2)
+        hk = w.key_cache[torch.from_numpy(ids_h.astype(np.int64)).to(dev)].cpu()
+        hv = w.value_cache[torch.from_numpy(ids_h.astype(np.int64)).to(dev)].cpu()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle_copy(hk, hv, small.tolist())
+            reps += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(alg_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{T} block copies in a host pool of the {2 * T} blocks "
+                                         f"they touch (the oracle also clones that pool), {reps} pass(es)",
+                               "seconds": round(dt, 2)}
+    elif not args.no_cpu_baseline:
         import oracle
         # host copy of the same rows; the pool holds just the blocks the
         # write touches (renumbered in first-touch order), so the sample
@@ -249,6 +284,14 @@ def main():
           f"kv={w.kv_bytes() / 1e9:.3f} GB (generated in {time.perf_counter() - t_gen:.1f}s)",
           file=sys.stderr, flush=True)
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.op != "decode":
         bench_write(args, w, dev)
         return
@@ -278,14 +321,6 @@ def main():
         if evs is not None:
             evs[2].record(stream)
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

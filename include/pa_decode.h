@@ -60,7 +60,9 @@ typedef enum {
     PA_ERR_SHAPE = 2,       /* negative / zero size, Hq % Hkv != 0, size overflow */
     PA_ERR_UNSUPPORTED = 3, /* dtype, head size or kernel choice not supported  */
     PA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned       */
-    PA_ERR_HIP = 5          /* the HIP runtime reported an error at launch      */
+    PA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch      */
+    PA_ERR_NO_BLOCKS = 6,   /* block pool: not enough free blocks (nothing changed) */
+    PA_ERR_BAD_ID = 7       /* block pool: unknown or released sequence / block id */
 } pa_status;
 
 /* Kernel families (pa_config.kernel). */
@@ -205,6 +207,26 @@ pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_
                        pa_dtype dtype, void *stream);
 
 /* Human-readable name of a status code (static storage). */
+/*
+ * pa_copy_blocks -- batched whole-block copy inside both caches, the copy step
+ * of copy-on-write (page "PagedAttention by hand", section "Memory Sharing
+ * (Copy-on-Write)": before a sequence writes into a block that other
+ * sequences still use, the block's contents are copied to a fresh block and
+ * the write goes to the copy).
+ *
+ *   pairs   [n][2] int32, device: pairs[i] = {src, dst}; block dst of both
+ *           caches becomes a copy of block src (all Hkv heads, all B slots)
+ *   key_cache, value_cache [NB][Hkv][B][D], device, updated in place
+ *
+ * Pairs with src or dst outside [0, NB), or src == dst, are skipped.  The dst
+ * blocks must be distinct and no dst may be another pair's src (a block pool
+ * never produces either); otherwise the result is unspecified.  Bits are
+ * copied unchanged.  Asynchronous on `stream`.  n = 0 is a no-op.
+ * Errors: PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (dtype), PA_ERR_NULL, PA_ERR_HIP.
+ */
+pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int n,
+                         int Hkv, int D, int B, int NB, pa_dtype dtype, void *stream);
+
 const char *pa_status_string(pa_status status);
 
 #ifdef __cplusplus

@@ -7,7 +7,9 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``decode`` wraps the plain fp64 C implementation in ``pa_oracle.c`` (gather the
 sequence's blocks through the block table into contiguous K / V, then standard
 max-subtracted softmax attention; see that file's header for the passages it
-follows).  ``build`` compiles it with gcc.
+follows).  ``build`` compiles it with gcc.  ``write_kv`` stores new tokens'
+rows into their slots; ``block_manager`` holds the free-list / reference-count
+/ copy-on-write bookkeeping and the whole-block copy, in plain Python.
 """
 from __future__ import annotations
 

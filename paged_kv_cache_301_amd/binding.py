@@ -17,12 +17,14 @@ import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpa_decode.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "pa_decode.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADER = os.path.join(INCLUDE, "pa_decode.h")
 
 # pa_dtype
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 # pa_status
-PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(6)
+(PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
+ PA_ERR_NO_BLOCKS, PA_ERR_BAD_ID) = range(8)
 # pa_kernel
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA = range(4)
 KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA}
@@ -82,16 +84,41 @@ def load():
     lib.pa_write_kv.argtypes = [_PTR] * 5 + [_INT] * 6 + [_PTR]
     lib.pa_append_kv.restype = _INT
     lib.pa_append_kv.argtypes = [_PTR] * 6 + [_INT] * 7 + [_PTR]
+    lib.pa_copy_blocks.restype = _INT
+    lib.pa_copy_blocks.argtypes = [_PTR] * 3 + [_INT] * 6 + [_PTR]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [_INT]
+    # host block pool
+    P, I32P = _PTR, ctypes.POINTER(ctypes.c_int32)
+    IP = ctypes.POINTER(_INT)
+    for name, res, args in [
+            ("pa_pool_create", _INT, [_INT, _INT, I32P, ctypes.POINTER(_PTR)]),
+            ("pa_pool_destroy", None, [P]),
+            ("pa_pool_num_free", _INT, [P]),
+            ("pa_pool_refcount", _INT, [P, _INT]),
+            ("pa_seq_create", _INT, [P, IP]),
+            ("pa_seq_fork", _INT, [P, _INT, IP]),
+            ("pa_seq_append", _INT, [P, _INT, _INT, I32P, I32P, I32P]),
+            ("pa_seq_append_batch", _INT, [P, IP, _INT, I32P, I32P, IP]),
+            ("pa_seq_release", _INT, [P, _INT]),
+            ("pa_seq_length", _INT, [P, _INT]),
+            ("pa_seq_num_blocks", _INT, [P, _INT]),
+            ("pa_pool_export", _INT, [P, IP, _INT, _INT, ctypes.c_int32, I32P, I32P])]:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
     _lib = lib
     return lib
 
 
 def header_functions():
-    """Names of the functions include/pa_decode.h declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, re.M)))
+    """Names of the functions the headers under include/ declare."""
+    import glob
+    names = set()
+    for path in sorted(glob.glob(os.path.join(INCLUDE, "*.h"))):
+        text = open(path).read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pa_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -227,6 +254,108 @@ def append_kv(key, value, block_tables, seq_lens, key_cache, value_cache, stream
                             seq_lens.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
                             S, Hkv, D, B, NB, block_tables.shape[1], _TORCH_TO_PA[key.dtype],
                             _stream_handle(stream, key.device)))
+
+
+def copy_blocks(key_cache, value_cache, pairs, stream=None):
+    """Copy whole blocks src -> dst in both caches (pairs: GPU int32 [n,2]).
+    In place on the caches."""
+    lib = load()
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("key_cache and value_cache must match")
+    if not (key_cache.is_cuda and value_cache.is_cuda and pairs.is_cuda):
+        raise ValueError("tensors must be on the GPU")
+    if key_cache.dim() != 4 or not (key_cache.is_contiguous() and value_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous [NB,Hkv,B,D]")
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise ValueError("pairs must be a contiguous int32 [n,2] tensor")
+    NB, Hkv, B, D = key_cache.shape
+    _check(lib.pa_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), pairs.data_ptr(),
+                              pairs.shape[0], Hkv, D, B, NB, _TORCH_TO_PA[key_cache.dtype],
+                              _stream_handle(stream, key_cache.device)))
+
+
+class BlockPool:
+    """Host block pool of the library (free stack, reference counts, block
+    tables, copy-on-write).  Thin wrapper: every operation is one C call."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            if len(free_order) != num_blocks:
+                raise ValueError("free_order must list every block once")
+            order = (ctypes.c_int32 * num_blocks)(*[int(b) for b in free_order])
+        _check(self._lib.pa_pool_create(num_blocks, block_size, order, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return self._lib.pa_pool_num_free(self._h)
+
+    def refcount(self, block: int) -> int:
+        return self._lib.pa_pool_refcount(self._h, block)
+
+    def create(self) -> int:
+        sid = ctypes.c_int()
+        _check(self._lib.pa_seq_create(self._h, ctypes.byref(sid)))
+        return sid.value
+
+    def fork(self, parent: int) -> int:
+        sid = ctypes.c_int()
+        _check(self._lib.pa_seq_fork(self._h, parent, ctypes.byref(sid)))
+        return sid.value
+
+    def append(self, seq: int, n: int = 1):
+        """Slots for the next n tokens and the copy-on-write pair (or None)."""
+        slots = (ctypes.c_int32 * max(n, 1))()
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.pa_seq_append(self._h, seq, n, slots, ctypes.byref(src), ctypes.byref(dst)))
+        return list(slots[:n]), (None if src.value < 0 else (src.value, dst.value))
+
+    def append_batch(self, seqs):
+        """One new token per sequence: (slots, [(src, dst), ...])."""
+        n = len(seqs)
+        ids = (ctypes.c_int * max(n, 1))(*seqs)
+        slots = (ctypes.c_int32 * max(n, 1))()
+        pairs = (ctypes.c_int32 * max(2 * n, 2))()
+        npairs = ctypes.c_int()
+        _check(self._lib.pa_seq_append_batch(self._h, ids, n, slots, pairs, ctypes.byref(npairs)))
+        k = npairs.value
+        return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(k)]
+
+    def release(self, seq: int):
+        _check(self._lib.pa_seq_release(self._h, seq))
+
+    def length(self, seq: int) -> int:
+        return self._lib.pa_seq_length(self._h, seq)
+
+    def num_blocks_of(self, seq: int) -> int:
+        return self._lib.pa_seq_num_blocks(self._h, seq)
+
+    def export(self, seqs, max_blocks: int, pad: int = 0):
+        """Block tables [n][max_blocks] and lengths [n] (host int32 tensors)."""
+        n = len(seqs)
+        tables = torch.empty((n, max_blocks), dtype=torch.int32)
+        lens = torch.empty((n,), dtype=torch.int32)
+        ids = (ctypes.c_int * max(n, 1))(*seqs)
+        I32P = ctypes.POINTER(ctypes.c_int32)
+        _check(self._lib.pa_pool_export(self._h, ids, n, max_blocks, pad,
+                                        ctypes.cast(tables.data_ptr(), I32P),
+                                        ctypes.cast(lens.data_ptr(), I32P)))
+        return tables, lens
 
 
 class PreparedCall:

@@ -39,7 +39,7 @@ def _hipcc() -> str:
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "pa_api.cpp")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(verbose: bool = False, save_temps: str | None = None) -> str:

@@ -283,6 +283,19 @@ pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int n,
+                         int Hkv, int D, int B, int NB, pa_dtype dtype, void *stream) {
+    if (n < 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0) return PA_ERR_SHAPE;
+    if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+    if (n == 0) return PA_OK;
+    if (!key_cache || !value_cache || !pairs) return PA_ERR_NULL;
+    const long long block_bytes = (long long)Hkv * B * D * dtype_size(dtype);
+    if (block_bytes > 65535LL * 4096) return PA_ERR_SHAPE;   // grid.y: 4 KiB pieces
+    const hipError_t err = pa::launch_copy_blocks(key_cache, value_cache, pairs, n, block_bytes,
+                                                  NB, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 const char *pa_status_string(pa_status status) {
     switch (status) {
     case PA_OK: return "PA_OK";
@@ -291,6 +304,8 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape, type or kernel not supported";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the block pool has too few free blocks";
+    case PA_ERR_BAD_ID: return "PA_ERR_BAD_ID: unknown or released sequence or block id";
     }
     return "unknown pa_status";
 }

@@ -41,6 +41,8 @@ hipError_t launch_kv_write(const void *key, const void *value, const int32_t *sl
                            const int32_t *block_tables, const int32_t *seq_lens,
                            void *key_cache, void *value_cache, int T, int Hkv, int D, int B,
                            int NB, int max_blocks, int esz, hipStream_t st);
+hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int n,
+                              long long block_bytes, int NB, hipStream_t st);
 
 // Tokens one loop iteration of the tiled kernels covers; partitions are
 // multiples of this.
