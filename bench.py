@@ -206,7 +206,8 @@ def bench_write(args, w, dev):
         "kernel_us": round(k_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(kernel, f"{args.op}_{args.workload}", w.B)},
     }
     if not args.no_cpu_baseline and args.op == "copy_blocks":
         from oracle.block_manager import copy_blocks as oracle_copy

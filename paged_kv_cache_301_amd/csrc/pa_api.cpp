@@ -290,7 +290,7 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pair
     if (n == 0) return PA_OK;
     if (!key_cache || !value_cache || !pairs) return PA_ERR_NULL;
     const long long block_bytes = (long long)Hkv * B * D * dtype_size(dtype);
-    if (block_bytes > 65535LL * 4096) return PA_ERR_SHAPE;   // grid.y: 4 KiB pieces
+    if (block_bytes > (1LL << 40)) return PA_ERR_SHAPE;
     const hipError_t err = pa::launch_copy_blocks(key_cache, value_cache, pairs, n, block_bytes,
                                                   NB, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;

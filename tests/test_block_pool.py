@@ -248,7 +248,8 @@ def test_copy_blocks_validation():
     assert lib.pa_copy_blocks(fake, fake, fake, 2, 2, 8, 4, 4, 5, None) == b.PA_ERR_UNSUPPORTED
     assert lib.pa_copy_blocks(fake, None, fake, 2, 2, 8, 4, 4, b.PA_F16, None) == b.PA_ERR_NULL
     assert lib.pa_copy_blocks(None, None, None, 0, 2, 8, 4, 4, b.PA_F16, None) == b.PA_OK
-    assert lib.pa_copy_blocks(fake, fake, fake, 1, 65536, 512, 16, 4, b.PA_F32, None) == b.PA_ERR_SHAPE
+    assert lib.pa_copy_blocks(fake, fake, fake, 1, 65536, 512, 65536, 4, b.PA_F32, None) == b.PA_ERR_SHAPE
+    assert lib.pa_copy_blocks(fake, fake, fake, 1, 2, 0, 4, 4, b.PA_F32, None) == b.PA_ERR_SHAPE
 
 
 # ------------------------------------------------------------ GPU
