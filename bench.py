@@ -35,8 +35,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha_7b",
-                    help="mha_small | mha_7b | gqa_70b | gqa_long (default: mha_7b, the batch-64 case)")
+                    help="mha_small | mha_7b | gqa_70b | gqa_long | mqa (default: mha_7b, the batch-64 case)")
     ap.add_argument("--block-size", type=int, default=None, help="override B (gqa_long sweeps 1/8/16/32)")
+    ap.add_argument("--q-heads", type=int, default=None, help="override Hq (e.g. mqa with 32 query heads)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--kv-reuse", choices=["on", "off"], default="off",
@@ -277,6 +278,8 @@ def main():
     over = {}
     if args.block_size:
         over["B"] = args.block_size
+    if args.q_heads:
+        over["Hq"] = args.q_heads
     t_gen = time.perf_counter()
     w = workloads.make_workload(args.workload, device=dev, poison=False, **over)
     torch.cuda.synchronize()

@@ -17,7 +17,7 @@ using pa::Args;
 // kAutoMaxParts partitions per context (long contexts: fewer, longer
 // partitions keep the combine pass and the partial results small), then
 // halved (down to kAutoPartitionFloor) while the grid would hold fewer than
-// kAutoMinItems (sequence, kv head, partition) items, so small batches still
+// kAutoMinItems waves over (sequence, kv head, partition) items, so small batches still
 // occupy 256 CUs.  Contexts of at most kAutoSinglePass tokens run in one pass.
 constexpr long long kAutoPartitionMin = 512;
 constexpr long long kAutoMaxParts = 32;
@@ -25,12 +25,13 @@ constexpr long long kAutoPartitionFloor = 64;
 constexpr long long kAutoMinItems = 4096;
 constexpr long long kAutoSinglePass = 256;
 
-long long auto_partition(int S, int Hkv, long long max_ctx) {
+// waves: waves per work-group (the matrix-core kernel runs ceil(G / 16)).
+long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
     if (max_ctx <= kAutoSinglePass) return max_ctx;
     long long part = kAutoPartitionMin;
     while (part * kAutoMaxParts < max_ctx) part *= 2;
     while (part > kAutoPartitionFloor &&
-           (long long)S * Hkv * ((max_ctx + part - 1) / part) < kAutoMinItems)
+           (long long)S * Hkv * waves * ((max_ctx + part - 1) / part) < kAutoMinItems)
         part /= 2;
     return part;
 }
@@ -70,7 +71,7 @@ bool supports_valu(int Hq, int Hkv, int D, int B, pa_dtype dt) {
 bool supports_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
     const int G = Hq / Hkv;
     return D == 128 && (dt == PA_F16 || dt == PA_BF16) && is_pow2(B) &&
-           (G == 4 || G == 8 || G == 16);
+           (G == 4 || G == 8 || G == 16 || G == 32 || G == 64);
 }
 
 // Largest partition whose block-table slice fits the LDS copy (the tiled
@@ -111,7 +112,8 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
     pa_plan p{};
     if (kernel != PA_KERNEL_GENERIC) {
         const long long cap = table_cap(kernel, B);
-        long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx);
+        const int waves = kernel == PA_KERNEL_MFMA ? (Hq / Hkv + 15) / 16 : 1;
+        long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx, waves);
         if (part >= max_ctx) {   // single pass: one partition covers any context
             part = ((max_ctx > 0 ? max_ctx : 1) + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;
         }

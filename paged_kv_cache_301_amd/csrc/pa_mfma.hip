@@ -6,8 +6,14 @@
 //     S^T [tokens x heads] = K [tokens x D]   . Q^T [D x heads]
 //     O^T [D x heads]     += V^T [D x tokens] . P^T [tokens x heads]
 // Both run on v_mfma_f32_16x16x32_{bf16,f16} with the head group padded to 16
-// columns.  One wave64 handles one (sequence, kv head, context partition); an
-// iteration covers 32 tokens (two 16-row score tiles, one 32-deep P.V step).
+// columns per wave.  One work-group handles one (sequence, kv head, context
+// partition) with W = ceil(G / 16) waves: wave w owns query heads 16 w .. 16 w
+// + 15 of the group (G = Hq with one kv head is multi-query attention).  An
+// iteration covers 32 W tokens: wave u loads the 32-token sub-tile u (two
+// 16-row score tiles, one 32-deep P.V step) and stages it in LDS; then every
+// wave runs the contractions for its own heads over all W sub-tiles, so each
+// K / V byte is read from HBM once for all G heads and each wave keeps a whole
+// sub-tile of loads in flight, as in the one-wave case.
 //
 // K and V arrive as whole token rows (pa_tile.h: full 128-byte lines per load
 // instruction) and are staged through LDS, from where each operand is read in
@@ -41,6 +47,7 @@ namespace pa {
 namespace {
 
 constexpr int kD = kHeadDim;
+constexpr float kRescaleSlack = 8.f;   // see mfma_subtile
 
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
@@ -100,61 +107,81 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint4 *lds_base, int byte_o
         (lds_i16x4 *)((lds_char *)lds_base + byte_off));
 }
 
-template <typename T, int G>
+template <typename T>
 struct MfmaState {
     f32x4 o[8];   // O^T, d-chunk n: rows 16n + 4g + r, column = head i
     float m;      // running max of head i (exp2 units), uniform over g
     float l;      // this lane's share of head i's weight sum
 };
 
-template <typename T, int G>
-__device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const KVTile &tile,
-                                             const typename Mfma<T>::Vec (&qf)[4],
-                                             uint4 *klds, uint4 *vlds, int t0, int t_end,
-                                             int g, int i, float scale_log2) {
-    using M = Mfma<T>;
-    using Vec = typename M::Vec;
-    // rows 4k + g, chunk i, to the swizzled LDS images
+// This wave's tile rows 4k + g, chunk i, to its swizzled LDS images.
+__device__ __forceinline__ void mfma_stage(const KVTile &tile, uint4 *klds, uint4 *vlds, int g,
+                                           int i) {
 #pragma unroll
     for (int k = 0; k < kTileLoads; ++k) {
         const int row = 4 * k + g;
         klds[row * 16 + (i ^ swz_k(row))] = tile.k[k];
         vlds[row * 16 + (i ^ swz_v(row))] = tile.v[k];
     }
-    __syncthreads();   // rows visible to every lane
+}
 
+// Scores, online softmax update and P.V for one staged 32-token sub-tile
+// starting at token t0 (which is < t_end).
+template <typename T>
+__device__ __forceinline__ void mfma_subtile(MfmaState<T> &st, const typename Mfma<T>::Vec (&qf)[4],
+                                             const uint4 *klds, const uint4 *vlds, int t0,
+                                             int t_end, int g, int i, float scale_log2) {
+    using M = Mfma<T>;
+    using Vec = typename M::Vec;
     // scores: A operand = chunk 4kk + g of row 16u + i (swizzle swz_k = i)
-    float x[8];
+    f32x4 acc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const uint4 a = klds[(16 * u + i) * 16 + ((4 * kk + g) ^ i)];
-            acc = M::mma(bitcast<Vec>(a), qf[kk], acc);
+            acc[u] = M::mma(bitcast<Vec>(a), qf[kk], acc[u]);
         }
+    }
+    float x[8];
+    if (t0 + 32 <= t_end) {   // uniform: the whole sub-tile is inside the context
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            x[4 * u + r] = (t0 + 16 * u + 4 * g + r < t_end) ? acc[r] * scale_log2 : kNegInf;
+        for (int j = 0; j < 8; ++j) x[j] = acc[j >> 2][j & 3] * scale_log2;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = (t0 + 16 * (j >> 2) + 4 * g + (j & 3) < t_end) ? acc[j >> 2][j & 3] * scale_log2
+                                                                  : kNegInf;
     }
     float mt = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
     mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float mn = fmaxf(st.m, mt);     // finite: token t0 is valid
-    const float alpha = fast_exp2(st.m - mn);
+    // The reference point st.m moves only when a head's maximum exceeds it by
+    // more than kRescaleSlack (log2 units; always on the first sub-tile, where
+    // st.m = -inf): otherwise the weights are taken against the stale value
+    // (p <= 2^kRescaleSlack, exact in fp32) and the rescale of O, which is most
+    // of a sub-tile's vector work, is skipped for the whole wave.  o / l and
+    // the partial triple (m, l, o) are the same quantities either way.
+    const bool grow = mt > st.m + kRescaleSlack;     // finite mt: token t0 is valid
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {    // uniform branch
+        const float mn = grow ? mt : st.m;
+        const float alpha = fast_exp2(st.m - mn);
+        st.l *= alpha;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+        st.m = mn;
+    }
     float p[8];
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(x[j] - mn);
+        p[j] = fast_exp2(x[j] - st.m);
         ps += p[j];
     }
-    st.l = st.l * alpha + ps;
-    st.m = mn;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+    st.l += ps;
     Vec phi, plo;
     split_probs<T>(p, phi, plo);
 
@@ -169,12 +196,30 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T, G> &st, const KVTile &
         st.o[n] = M::mma(va, phi, st.o[n]);
         st.o[n] = M::mma(va, plo, st.o[n]);
     }
+}
+
+// One iteration: every wave stages its sub-tile, then runs all W sub-tiles
+// that start before t_end.  t0 = first token of the iteration.
+template <typename T, int W>
+__device__ __forceinline__ void mfma_compute(MfmaState<T> &st, const KVTile &tile,
+                                             const typename Mfma<T>::Vec (&qf)[4],
+                                             uint4 (*klds)[32 * 16], uint4 (*vlds)[32 * 16],
+                                             int w, int t0, int t_end, int g, int i,
+                                             float scale_log2) {
+    mfma_stage(tile, klds[w], vlds[w], g, i);
+    __syncthreads();   // rows visible to every lane of every wave
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+        if (t0 + 32 * u >= t_end) break;   // uniform: the rest of the iteration is past the end
+        mfma_subtile<T>(st, qf, klds[u], vlds[u], t0 + 32 * u, t_end, g, i, scale_log2);
+    }
     __syncthreads();   // reads done before the next iteration overwrites LDS
 }
 
 template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
-__global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
+__global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
+    constexpr int W = (G + 15) / 16;          // waves per work-group = 32-token sub-tiles per iteration
     int s, kvh, p;
     if (a.compact) {
         // 1-D grid over the live items, partition-major (see pa_sched.h)
@@ -192,7 +237,8 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
         s = blockIdx.x / a.Hkv;
         p = blockIdx.y;
     }
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15;
     const int g = lane >> 4;
 
@@ -202,14 +248,15 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     const int t_end = min(L, t_begin + a.part_tokens);
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
-    __shared__ uint4 klds[32 * 16];
-    __shared__ uint4 vlds[32 * 16];
+    __shared__ uint4 klds[W][32 * 16];
+    __shared__ uint4 vlds[W][32 * 16];
     __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
 
-    // Q^T fragments; columns past the group are zero
+    // Q^T fragments of this wave's heads; columns past the group are zero
     Vec qf[4];
-    const bool head_ok = i < G;
-    const T *qrow = static_cast<const T *>(a.query) + ((size_t)s * a.Hq + kvh * G + (head_ok ? i : 0)) * kD;
+    const int hg = 16 * w + i;                // head within the group
+    const bool head_ok = hg < G;
+    const T *qrow = static_cast<const T *>(a.query) + ((size_t)s * a.Hq + kvh * G + (head_ok ? hg : 0)) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         uint4 w = *reinterpret_cast<const uint4 *>(qrow + 8 * g + 32 * kk);
@@ -217,7 +264,7 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
         qf[kk] = bitcast<Vec>(w);
     }
 
-    MfmaState<T, G> st;
+    MfmaState<T> st;
 #pragma unroll
     for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m = kNegInf;
@@ -237,26 +284,28 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
         ctx.tv.j0 = t_begin >> a.log2B;
         ctx.tbl = tbl;
         if constexpr (!SCALAR) {
-            stage_table(tbl, ctx.tv, t_begin, t_end, lane, 64);
+            stage_table(tbl, ctx.tv, t_begin, t_end, threadIdx.x, 64 * W);
             __syncthreads();
         }
 
-        const int niter = (t_end - t_begin + 31) >> 5;
+        constexpr int kIter = 32 * W;          // tokens per iteration
+        const int niter = (t_end - t_begin + kIter - 1) / kIter;
+        const int tw = t_begin + 32 * w;       // this wave's sub-tile of iteration 0
         KVTile ta, tb;
-        ctx.load(ta, t_begin);
+        ctx.load(ta, tw);
         // The scheduling barriers keep each prefetch ahead of the wait for
         // the tile computed next; without them the compiler sinks the loads
         // below that wait and the wave never has two tiles in flight.
         for (int it = 0; it < niter; it += 2) {
-            const int t0 = t_begin + 32 * it;
-            ctx.load(tb, t0 + 32);
+            const int t0 = t_begin + kIter * it;
+            ctx.load(tb, tw + kIter * (it + 1));
             __builtin_amdgcn_sched_barrier(0);
-            mfma_compute<T, G>(st, ta, qf, klds, vlds, t0, t_end, g, i, a.scale_log2);
+            mfma_compute<T, W>(st, ta, qf, klds, vlds, w, t0, t_end, g, i, a.scale_log2);
             __builtin_amdgcn_sched_barrier(0);
-            ctx.load(ta, t0 + 64);
+            ctx.load(ta, tw + kIter * (it + 2));
             __builtin_amdgcn_sched_barrier(0);
             if (it + 1 < niter)
-                mfma_compute<T, G>(st, tb, qf, klds, vlds, t0 + 32, t_end, g, i, a.scale_log2);
+                mfma_compute<T, W>(st, tb, qf, klds, vlds, w, t0 + kIter, t_end, g, i, a.scale_log2);
             __builtin_amdgcn_sched_barrier(0);
         }
         st.l += shfl_xor(st.l, 16);
@@ -264,7 +313,7 @@ __global__ __launch_bounds__(64, 2) void mfma_kernel(Args a) {
     }
 
     if (!head_ok) return;
-    const int head = kvh * G + i;
+    const int head = kvh * G + hg;
     if (nparts <= 1) {
         const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
 #pragma unroll
@@ -291,10 +340,11 @@ template <typename T, typename OutT, int G, bool STREAM>
 void launch_gs(const Args &a, hipStream_t st) {
     const dim3 grid = a.compact ? dim3((unsigned)((long long)a.Hkv * a.S * a.max_parts))
                                 : dim3(a.Hkv * a.S, a.max_parts);
+    const dim3 block(64 * ((G + 15) / 16));
     if (a.B % 4 == 0)
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, STREAM>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, STREAM>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, STREAM>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, STREAM>), grid, block, 0, st, a);
 }
 
 template <typename T, typename OutT, int G>
@@ -310,6 +360,8 @@ hipError_t launch_t(const Args &a, hipStream_t st) {
     case 4: return launch_g<T, OutT, 4>(a, st);
     case 8: return launch_g<T, OutT, 8>(a, st);
     case 16: return launch_g<T, OutT, 16>(a, st);
+    case 32: return launch_g<T, OutT, 32>(a, st);
+    case 64: return launch_g<T, OutT, 64>(a, st);
     }
     return hipErrorInvalidValue;
 }

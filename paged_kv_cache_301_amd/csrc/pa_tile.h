@@ -21,10 +21,14 @@ constexpr int kHeadDim = 128;      // elements per token row
 constexpr int kRowBytes = 256;     // bytes per token row (16-bit elements)
 constexpr int kTileLoads = 8;      // load instructions per operand per iteration
 
-struct KVTile {
-    uint4 k[kTileLoads];   // chunk (lane % 16) of token 4 k + lane / 16
-    uint4 v[kTileLoads];
+// N load instructions per operand: the whole 32-token tile (N = 8), or a
+// 1/W share of it when W waves of a work-group load one tile together.
+template <int N = kTileLoads>
+struct KVTileN {
+    uint4 k[N];   // chunk (lane % 16) of token 4 (k0 + k) + lane / 16
+    uint4 v[N];
 };
+using KVTile = KVTileN<>;
 
 template <bool SCALAR, bool STREAM>
 struct TileLoader {
@@ -37,10 +41,12 @@ struct TileLoader {
     TableView tv;
     const int32_t *tbl;
 
-    __device__ __forceinline__ void load(KVTile &tile, int t0) const {
+    // Rows 4 (k0 + k) + g, k < N, of the tile starting at token t0.
+    template <int N>
+    __device__ __forceinline__ void load(KVTileN<N> &tile, int t0, int k0 = 0) const {
 #pragma unroll
-        for (int k = 0; k < kTileLoads; ++k) {
-            const int t = min(t0 + 4 * k + g, t_end - 1);
+        for (int k = 0; k < N; ++k) {
+            const int t = min(t0 + 4 * (k0 + k) + g, t_end - 1);
             const int phys = phys_block<SCALAR>(tv, tbl, t);
             const size_t off = (size_t)phys * block_bytes + (size_t)(t & bmask) * kRowBytes;
             tile.k[k] = load_kv16<STREAM>(kbase + off);

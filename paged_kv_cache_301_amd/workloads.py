@@ -80,6 +80,11 @@ SPECS = {
                              dtype="bf16", lens=("uniform", 16384, 32768),
                              max_len=32768, pool=("free", 0.25), seed=5,
                              prefix_tokens=4096),
+    # multi-query: 256 seqs, 64 q heads on one kv head, D=128, B=16, bf16,
+    # L ~ U[512, 4096], pool = need + 25 %.
+    "mqa": WorkloadSpec("mqa", S=256, Hq=64, Hkv=1, D=128, B=16, dtype="bf16",
+                        lens=("uniform", 512, 4096), max_len=4096, pool=("free", 0.25),
+                        seed=6),
 }
 
 

@@ -89,6 +89,10 @@ def test_plans():
     # block size 1 with the matrix-core kernel: the table slice fits LDS
     p = b.plan(16, 32, 8, 128, 1, 10, 32768, torch.bfloat16, partition_tokens=4096)
     assert p["partition_tokens"] <= 1024
+    # groups of 32 / 64 (multi-query) run on the matrix cores, wider ones do not
+    for Hq, Hkv in ((64, 1), (32, 1), (64, 2)):
+        assert b.plan(256, Hq, Hkv, 128, 16, 100, 256, torch.bfloat16)["kernel"] == b.KERNEL_MFMA
+    assert b.plan(4, 128, 1, 128, 16, 100, 256, torch.bfloat16)["kernel"] == b.KERNEL_GENERIC
     # generic ignores partitioning
     p = b.plan(2, 4, 2, 96, 3, 10, 50, torch.bfloat16)
     assert p["kernel"] == b.KERNEL_GENERIC and p["split"] == 0

@@ -95,6 +95,12 @@ SMALL = [
     ("mfma", "bf16", 16, 4, 2, 32),
     ("mfma", "bf16", 32, 2, 32, 64),
     ("mfma", "bf16", 16, 1, 64, 0),
+    # groups wider than 16: several waves per work-group (MQA when Hkv = 1)
+    ("mfma", "bf16", 32, 1, 16, 0),
+    ("mfma", "f16", 64, 1, 16, 64),
+    ("mfma", "bf16", 64, 2, 8, 96),
+    ("mfma", "bf16", 64, 1, 1, 64),
+    ("mfma", "f16", 32, 1, 2, 32),
 ]
 
 
@@ -131,7 +137,7 @@ def test_zero_length_rows_are_zero(kernel):
 
 NEEDLE_KERNELS = [("generic", 8, 2, 16, 0), ("valu", 8, 8, 16, 64), ("valu", 8, 8, 1, 64),
                   ("valu", 8, 4, 8, 0), ("mfma", 16, 2, 16, 64), ("mfma", 16, 4, 1, 96),
-                  ("mfma", 32, 4, 8, 0)]
+                  ("mfma", 32, 4, 8, 0), ("mfma", 64, 1, 16, 64), ("mfma", 64, 2, 1, 0)]
 
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,B,part", NEEDLE_KERNELS)
@@ -178,7 +184,8 @@ def test_needle_bit_exact(kernel, Hq, Hkv, B, part):
 
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,B,part", [("valu", 8, 8, 16, 64), ("mfma", 16, 2, 16, 64),
-                                                  ("mfma", 16, 4, 1, 64), ("generic", 4, 2, 16, 0)])
+                                                  ("mfma", 16, 4, 1, 64), ("generic", 4, 2, 16, 0),
+                                                  ("mfma", 64, 1, 16, 64)])
 def test_relabel_poison_determinism(kernel, Hq, Hkv, B, part):
     say(f"case: relabel/poison/determinism {kernel} B={B}")
     spec = workloads.WorkloadSpec("perm", S=4, Hq=Hq, Hkv=Hkv, D=128, B=B, dtype="bf16",
@@ -205,10 +212,11 @@ def test_relabel_poison_determinism(kernel, Hq, Hkv, B, part):
     assert torch.equal(a, d), "relabelling physical blocks changed the output"
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma", "mfma64"])
 def test_stages_equal_one_call(kernel):
     say(f"case: staged partitions+combine vs one call, {kernel}")
-    Hq, Hkv = (8, 8) if kernel == "valu" else (16, 2)
+    Hq, Hkv = {"valu": (8, 8), "mfma": (16, 2), "mfma64": (64, 1)}[kernel]
+    kernel = kernel[:4] if kernel == "mfma64" else kernel
     spec = workloads.WorkloadSpec("stages", S=3, Hq=Hq, Hkv=Hkv, D=128, B=16, dtype="bf16",
                                   lens=("fixed", (33, 300, 900)), max_len=960,
                                   pool=("free", 0.3), seed=12)
@@ -229,7 +237,8 @@ def test_stages_equal_one_call(kernel):
 # --------------------------------------------------- benchmark-sized workloads
 
 FULL = [("mha_small", {}), ("mha_7b", {}), ("gqa_70b", {}), ("gqa_long", {"B": 16}),
-        ("gqa_long", {"B": 1}), ("gqa_long", {"B": 8}), ("gqa_long", {"B": 32})]
+        ("gqa_long", {"B": 1}), ("gqa_long", {"B": 8}), ("gqa_long", {"B": 32}),
+        ("mqa", {}), ("mqa", {"Hq": 32})]
 
 
 @pytest.mark.parametrize("name,over", FULL)
@@ -256,7 +265,7 @@ def test_full_size_sampled(name, over):
 
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,B", [("valu", 8, 8, 16), ("valu", 8, 8, 1), ("mfma", 16, 2, 16),
-                                             ("mfma", 16, 4, 8)])
+                                             ("mfma", 16, 4, 8), ("mfma", 32, 1, 16)])
 def test_kv_reuse_hint_is_bit_identical(kernel, Hq, Hkv, B):
     """Streamed and cached K/V loads differ only in cache policy."""
     say(f"case: kv_reuse on/off {kernel} B={B}")
@@ -271,7 +280,8 @@ def test_kv_reuse_hint_is_bit_identical(kernel, Hq, Hkv, B):
 
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,S", [("valu", 4, 4, 700), ("mfma", 16, 2, 700),
-                                             ("valu", 2, 2, 1100), ("mfma", 8, 2, 1100)])
+                                             ("valu", 2, 2, 1100), ("mfma", 8, 2, 1100),
+                                             ("mfma", 64, 1, 700), ("mfma", 32, 1, 1100)])
 def test_many_sequences(kernel, Hq, Hkv, S):
     """Batches beyond one wave's worth of lengths (live-item decode over
     several register chunks) and beyond 1024 sequences (rectangular grid)."""
