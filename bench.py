@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense matrix-core peaks
 METRIC = "Paged decode attention: achieved KV-read GB/s and % of HBM peak; seqs/s"
 KERNEL_NAMES = {0: "auto", 1: "generic", 2: "valu", 3: "mfma"}
 
@@ -47,11 +48,14 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the kernel-source hash used to match counter records, then exit")
-    ap.add_argument("--op", choices=["decode", "write_kv", "append_kv", "copy_blocks"],
+    ap.add_argument("--op", choices=["decode", "write_kv", "append_kv", "copy_blocks", "prefill"],
                     default="decode",
                     help="decode (default): the attention step; write_kv: store a prompt chunk's "
                          "K/V through a slot mapping; append_kv: store one new token per sequence; "
-                         "copy_blocks: copy-on-write copies of --pairs whole blocks")
+                         "copy_blocks: copy-on-write copies of --pairs whole blocks; "
+                         "prefill: causal attention of --new-tokens per sequence (workload 'prefill')")
+    ap.add_argument("--new-tokens", type=int, default=0,
+                    help="prefill: new tokens per sequence (default: the workload's chunk)")
     ap.add_argument("--pairs", type=int, default=1024, help="copy_blocks: blocks copied per step")
     ap.add_argument("--tokens", type=int, default=16384,
                     help="write_kv: tokens in the chunk")
@@ -255,6 +259,106 @@ def bench_write(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_prefill(args, dev):
+    """Causal multi-token step: every sequence's chunk of new tokens against its
+    cache (all rows, all heads); matrix-core bound."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_301_amd import binding, workloads
+    over = {}
+    if args.block_size:
+        over["B"] = args.block_size
+    if args.q_heads:
+        over["Hq"] = args.q_heads
+    name = args.workload if args.workload in workloads.PREFILL_NEW else "prefill"
+    pw = workloads.make_prefill_workload(name, args.new_tokens or None, device=dev, **over)
+    w = pw.base
+    torch.cuda.synchronize()
+    plan = binding.plan_prefill(w.S, pw.T, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks,
+                                pw.max_query_len, w.dtype, kernel=args.kernel,
+                                partition_tokens=args.partition_tokens)
+    ws = (torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+          if plan["workspace_bytes"] else None)
+    out = torch.empty_like(pw.query)
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(max_query_len=pw.max_query_len, kernel=args.kernel,
+              partition_tokens=args.partition_tokens, workspace=ws, stream=stream)
+    a = (pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, pw.query_start, w.scale, out)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        binding.prefill(*a, stages=binding.STAGE_PARTITIONS, **kw)
+        if evs is not None:
+            evs[1].record(stream)
+        if plan["split"]:
+            binding.prefill(*a, stages=binding.STAGE_COMBINE, **kw)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_ms = wall * 1e3 / args.steps
+    flops = pw.flops()
+    tf = flops / (step_ms * 1e-3) / 1e12
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    kname = {1: "generic", 3: "mfma"}[plan["kernel"]]
+    dts = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype]
+    peak = MFMA_PEAK_TFLOPS.get(dts, 157.3)
+    print(f"[bench] prefill: S={w.S} T={pw.T} Hq={w.Hq} Hkv={w.Hkv} B={w.B} ctx={int(w.lens.sum())} "
+          f"plan {plan}; kernel {k_ms * 1e3:.1f} us, combine {c_ms * 1e3:.1f} us, step {step_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    res = {
+        "metric": "Paged causal multi-token attention (chunked prefill): TFLOP/s",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dts, "data": "synthetic",
+        "config": {"workload": f"prefill_{name}", "S": w.S, "T": pw.T, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "D": w.D, "B": w.B, "context_tokens": int(w.lens.sum()),
+                   "new_tokens_per_seq": int(pw.max_query_len), "flops": flops, "kernel": kname,
+                   "partition_tokens": plan["partition_tokens"], "split": bool(plan["split"])},
+        "kernel_us": {"partitions": round(k_ms * 1e3, 2), "combine": round(c_ms * 1e3, 2)},
+        "roofline": {"bound": "mfma", "kernel": f"pa_prefill_{kname}", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(f"pa_prefill_{kname}", f"prefill_{name}", w.B)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = list(range(w.Hq))                   # the first query row, all heads
+        oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                       pw.query_start, w.scale, rows=rows)
+        qs = pw.query_start.cpu().numpy()
+        # sample: the first rows of sequence 0 until ~cpu_seconds of work
+        n0 = int(qs[1])
+        t0 = time.perf_counter()
+        oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                       pw.query_start, w.scale, rows=rows)
+        t_one = max(time.perf_counter() - t0, 1e-6)
+        nrows = max(1, min(n0, int(args.cpu_seconds / t_one)))
+        rows = list(range(nrows * w.Hq))
+        t0 = time.perf_counter()
+        oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                       pw.query_start, w.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        L0, n_0 = int(w.lens[0]), n0
+        toks = sum(L0 - n_0 + k + 1 for k in range(nrows))
+        res["cpu_baseline"] = {"value": round(4 * w.D * w.Hq * toks / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"first {nrows} query rows of sequence 0, all heads",
+                               "seconds": round(dt, 2)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.print_source_sha:
@@ -275,6 +379,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.op == "prefill":
+        bench_prefill(args, dev)
+        return
     over = {}
     if args.block_size:
         over["B"] = args.block_size

@@ -59,6 +59,13 @@ def _load():
         lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_prefill.restype = ctypes.c_int
+        lib.oracle_prefill.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_int]
         lib.oracle_write_kv.restype = ctypes.c_longlong
         lib.oracle_write_kv.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -117,6 +124,44 @@ def write_kv(key, value, slot_mapping, key_cache, value_cache, inplace=False):
     n = _load().oracle_write_kv(k.data_ptr(), v.data_ptr(), sm.data_ptr(), kc.data_ptr(),
                                 vc.data_ptr(), T, Hkv, D, B, NB, k.element_size())
     return kc, vc, int(n)
+
+
+def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start,
+            scale: float, rows=None) -> np.ndarray:
+    """fp64 causal attention of several new tokens per sequence.
+
+    query [T,Hq,D] (rows grouped by sequence); query_start [S+1] int32; the
+    other arguments as in ``decode`` (seq_lens count the new tokens).  Row
+    query_start[s] + k attends tokens 0 .. seq_lens[s] - n_s + k.  Returns
+    float64 [T,Hq,D], or [len(rows),D] for flat (t * Hq + h) ``rows``.
+    """
+    import torch
+    q, kc, vc = _host(query), _host(key_cache), _host(value_cache)
+    bt = _host(block_tables).to(torch.int32)
+    sl = _host(seq_lens).to(torch.int32)
+    qs = _host(query_start).to(torch.int32)
+    if not (q.dtype == kc.dtype == vc.dtype):
+        raise TypeError("query, key_cache and value_cache must share one dtype")
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = kc.shape
+    S = sl.shape[0]
+    if D2 != D or vc.shape != kc.shape or qs.shape != (S + 1,):
+        raise ValueError("shapes do not match")
+    max_blocks = bt.shape[1] if bt.dim() == 2 else 0
+    if rows is None:
+        rows_arr, nrows = None, T * Hq
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(list(rows), dtype=np.int32))
+        nrows = int(rows_arr.size)
+    out = np.zeros((nrows, D), dtype=np.float64)
+    rc = _load().oracle_prefill(
+        q.data_ptr(), kc.data_ptr(), vc.data_ptr(), bt.data_ptr(), sl.data_ptr(),
+        qs.data_ptr(), float(scale), out.ctypes.data, S, T, Hq, Hkv, D, B, NB,
+        max_blocks, _dtype_code(q),
+        None if rows_arr is None else rows_arr.ctypes.data, nrows)
+    if rc != 0:
+        raise ValueError(f"oracle_prefill rejected its arguments (code {rc})")
+    return out.reshape(T, Hq, D) if rows is None else out
 
 
 def decode(query, key_cache, value_cache, block_tables, seq_lens, scale: float,

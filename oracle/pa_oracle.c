@@ -86,18 +86,19 @@ static double load_elem(const void *base, size_t i, int dtype)
 }
 
 /*
- * One output row: sequence s, query head h.  Writes D doubles to o.
- * Returns ORACLE_ENOMEM if the gather buffers cannot be allocated.
+ * One output row: query row qrow (query[qrow][h]) attending the first n
+ * tokens of sequence s, query head h.  Writes D doubles to o.  Decode calls it
+ * with qrow = s and n = seq_lens[s].  Returns ORACLE_ENOMEM if the gather
+ * buffers cannot be allocated.
  */
-static int decode_row(const void *query, const void *key_cache,
+static int attend_row(const void *query, const void *key_cache,
                       const void *value_cache, const int32_t *block_tables,
-                      const int32_t *seq_lens, double scale, double *o,
+                      int qrow, int n, double scale, double *o,
                       int s, int h, int Hq, int Hkv, int D, int B,
                       int max_blocks, int dtype)
 {
     int G = Hq / Hkv;
     int g = h / G;                   /* kv head shared by this query head */
-    int n = seq_lens[s];             /* tokens in context */
 
     for (int d = 0; d < D; ++d) o[d] = 0.0;
     if (n <= 0) return ORACLE_OK;
@@ -128,7 +129,7 @@ static int decode_row(const void *query, const void *key_cache,
 
     /* Step 2: scores x_t = scale * q . K_t. */
     for (int d = 0; d < D; ++d)
-        qv[d] = load_elem(query, ((size_t)s * Hq + h) * D + d, dtype);
+        qv[d] = load_elem(query, ((size_t)qrow * Hq + h) * D + d, dtype);
     for (int tt = 0; tt < n; ++tt) {
         double acc = 0.0;
         for (int d = 0; d < D; ++d) acc += qv[d] * K[(size_t)tt * D + d];
@@ -194,9 +195,76 @@ int oracle_decode(const void *query, const void *key_cache,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < nrows; ++r) {
         int row = rows ? rows[r] : r;
-        int rc = decode_row(query, key_cache, value_cache, block_tables,
-                            seq_lens, scale, out + (size_t)r * D,
-                            row / Hq, row % Hq, Hq, Hkv, D, B, max_blocks, dtype);
+        int s = row / Hq;
+        int rc = attend_row(query, key_cache, value_cache, block_tables,
+                            s, seq_lens[s], scale, out + (size_t)r * D,
+                            s, row % Hq, Hq, Hkv, D, B, max_blocks, dtype);
+        if (rc != ORACLE_OK) {
+#pragma omp atomic write
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/*
+ * oracle_prefill -- several new tokens per sequence, causal, in fp64.
+ *
+ * Glossary "PagedAttention", section "How It Works": query i attends the
+ * logical blocks up to ceil(i / B), i.e. (token-level reading) every token up
+ * to and including its own position, the last block cut there.  Sequence s
+ * owns query rows query_start[s] .. query_start[s+1]-1, the last
+ * n_s = query_start[s+1] - query_start[s] of its L_s = seq_lens[s] tokens;
+ * row query_start[s] + k sits at position L_s - n_s + k and attends tokens
+ * 0 .. L_s - n_s + k.  Each output row is the decode computation (gather,
+ * then standard attention) over that many tokens.
+ *
+ *   query [T][Hq][D], out [nrows][D] doubles; row r of out is query row
+ *   rows[r] / Hq, head rows[r] % Hq (rows NULL: all T * Hq rows in order).
+ * Returns ORACLE_EINVAL for inconsistent sizes or offsets, ORACLE_ENOMEM.
+ */
+int oracle_prefill(const void *query, const void *key_cache,
+                   const void *value_cache, const int32_t *block_tables,
+                   const int32_t *seq_lens, const int32_t *query_start,
+                   double scale, double *out, int S, int T, int Hq, int Hkv,
+                   int D, int B, int NB, int max_blocks, int dtype,
+                   const int32_t *rows, int nrows)
+{
+    if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 ||
+        B <= 0 || NB <= 0 || max_blocks < 0 || nrows < 0)
+        return ORACLE_EINVAL;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+        return ORACLE_EINVAL;
+    if (!rows && nrows != T * Hq) return ORACLE_EINVAL;
+    if (query_start[0] != 0 || query_start[S] != T) return ORACLE_EINVAL;
+    for (int s = 0; s < S; ++s) {
+        int n = query_start[s + 1] - query_start[s];
+        int L = seq_lens[s];
+        if (n < 0 || (n > 0 && (L < n || (long long)L > (long long)max_blocks * B)))
+            return ORACLE_EINVAL;
+        if (n > 0)
+            for (int j = 0; j < (L + B - 1) / B; ++j) {
+                int p = block_tables[(size_t)s * max_blocks + j];
+                if (p < 0 || p >= NB) return ORACLE_EINVAL;
+            }
+    }
+    for (int r = 0; r < nrows; ++r) {
+        int row = rows ? rows[r] : r;
+        if (row < 0 || row >= T * Hq) return ORACLE_EINVAL;
+    }
+
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        int row = rows ? rows[r] : r;
+        int t = row / Hq, h = row % Hq;
+        int s = 0;                        /* the sequence owning query row t */
+        while (query_start[s + 1] <= t) ++s;
+        int n = query_start[s + 1] - query_start[s];
+        int pos = seq_lens[s] - n + (t - query_start[s]);
+        int rc = attend_row(query, key_cache, value_cache, block_tables,
+                            t, pos + 1, scale, out + (size_t)r * D,
+                            s, h, Hq, Hkv, D, B, max_blocks, dtype);
         if (rc != ORACLE_OK) {
 #pragma omp atomic write
             status = rc;

@@ -84,6 +84,12 @@ def load():
     lib.pa_write_kv.argtypes = [_PTR] * 5 + [_INT] * 6 + [_PTR]
     lib.pa_append_kv.restype = _INT
     lib.pa_append_kv.argtypes = [_PTR] * 6 + [_INT] * 7 + [_PTR]
+    mq_shape = [_INT] * 9 + [_INT, _INT]  # S T Hq Hkv D B NB max_blocks max_query_len dtype out_dtype
+    lib.pa_prefill_plan.restype = _INT
+    lib.pa_prefill_plan.argtypes = mq_shape + [ctypes.POINTER(PaConfig), ctypes.POINTER(PaPlan)]
+    lib.pa_prefill.restype = _INT
+    lib.pa_prefill.argtypes = ([_PTR] * 6 + [ctypes.c_float, _PTR] + mq_shape +
+                               [ctypes.POINTER(PaConfig), _PTR, ctypes.c_size_t, _PTR])
     lib.pa_copy_blocks.restype = _INT
     lib.pa_copy_blocks.argtypes = [_PTR] * 3 + [_INT] * 6 + [_PTR]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -204,6 +210,81 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
                             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
                             out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr, ws_bytes, st))
     return out
+
+
+def plan_prefill(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype, out_dtype=None, *,
+                 kernel="auto", partition_tokens=0, stages=0, kv_reuse=False) -> dict:
+    """Resolve the plan of a multi-token causal call (host only)."""
+    dt = _TORCH_TO_PA.get(dtype, dtype)
+    odt = dt if out_dtype is None else _TORCH_TO_PA.get(out_dtype, out_dtype)
+    p = PaPlan()
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    _check(load().pa_prefill_plan(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dt, odt,
+                                  ctypes.byref(cfg), ctypes.byref(p)))
+    return p.as_dict()
+
+
+def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start, scale,
+            out=None, *, max_query_len: Optional[int] = None, out_dtype=None, kernel="auto",
+            partition_tokens: int = 0, stages: int = 0, kv_reuse: bool = False,
+            workspace=None, stream=None) -> torch.Tensor:
+    """Causal attention of several new tokens per sequence: out[T,Hq,D] from
+    query[T,Hq,D] (rows grouped by sequence, query_start[S+1] int32), the
+    paged K/V pools and block_tables / seq_lens (lengths count the new
+    tokens).  ``max_query_len`` (the largest n_s) is read back from
+    query_start when not given, which synchronises the stream."""
+    lib = load()
+    for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_start", query_start)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for t in (block_tables, seq_lens, query_start):
+        if t.dtype != torch.int32:
+            raise TypeError("block_tables, seq_lens and query_start must be int32")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query, key_cache and value_cache must share one dtype")
+    if value_cache.shape != key_cache.shape:
+        raise ValueError("key_cache and value_cache shapes differ")
+    S = seq_lens.shape[0]
+    if query_start.shape != (S + 1,) or block_tables.shape[0] != S:
+        raise ValueError("query_start / block_tables do not match seq_lens")
+    T, Hq, D = query.shape
+    NB, Hkv, B, D2 = key_cache.shape
+    if D2 != D:
+        raise ValueError("query and cache head sizes differ")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if S else 0
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else query.dtype
+    if out is None:
+        out = torch.empty(query.shape, dtype=out_dtype, device=query.device)
+    elif out.shape != query.shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [T,Hq,D] tensor of out_dtype")
+    shape = (S, T, Hq, Hkv, D, B, NB, block_tables.shape[1], int(max_query_len),
+             _TORCH_TO_PA[query.dtype], _TORCH_TO_PA[out_dtype])
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    p = PaPlan()
+    _check(lib.pa_prefill_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
+    ws_ptr, ws_bytes = None, 0
+    if p.workspace_bytes:
+        if workspace is None:
+            workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=query.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.pa_prefill(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                          block_tables.data_ptr(), seq_lens.data_ptr(), query_start.data_ptr(),
+                          float(scale), out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr,
+                          ws_bytes, _stream_handle(stream, query.device)))
+    return out
+
+
+def prefill_workload(pw, **kw) -> torch.Tensor:
+    """``prefill`` on a PrefillWorkload (see workloads.make_prefill_workload)."""
+    w = pw.base
+    return prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                   pw.query_start, w.scale, max_query_len=pw.max_query_len, **kw)
 
 
 def _stream_handle(stream, device):

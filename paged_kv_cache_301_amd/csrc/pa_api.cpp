@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "pa_internal.h"
+#include "pa_prefill.h"
 
 namespace {
 
@@ -151,6 +152,88 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// ---------------------------------------------------------------- multi-token
+
+bool supports_prefill_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
+    const int G = Hq / Hkv;
+    return D == 128 && (dt == PA_F16 || dt == PA_BF16) && is_pow2(B) &&
+           (G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32 || G == 64);
+}
+
+// Work-groups below which the automatic plan splits contexts: the grid then
+// holds fewer than two four-wave groups per CU.
+constexpr long long kPrefillMinGroups = 1024;
+
+pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                            int max_query_len, pa_dtype dtype, pa_dtype out_dtype,
+                            const pa_config *cfg, pa_plan *plan, int *q_blocks) {
+    pa_status st = validate_shape(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype);
+    if (st != PA_OK) return st;
+    if (T < 0 || max_query_len < 0 || T > 65535) return PA_ERR_SHAPE;   // rows are grid y
+    if (T > 0 && S > 0 && max_query_len == 0) return PA_ERR_SHAPE;
+    if ((long long)T * Hq > INT_MAX) return PA_ERR_SHAPE;
+    int kernel = cfg ? cfg->kernel : PA_KERNEL_AUTO;
+    const int req = cfg ? cfg->partition_tokens : 0;
+    if (req < 0 || (req > 0 && req % pa::kTileTokens != 0)) return PA_ERR_SHAPE;
+    if (cfg && (cfg->stages < 0 || cfg->stages > PA_STAGE_ALL)) return PA_ERR_SHAPE;
+    switch (kernel) {
+    case PA_KERNEL_AUTO:
+        kernel = supports_prefill_mfma(Hq, Hkv, D, B, dtype) ? PA_KERNEL_MFMA : PA_KERNEL_GENERIC;
+        break;
+    case PA_KERNEL_GENERIC:
+        break;
+    case PA_KERNEL_MFMA:
+        if (!supports_prefill_mfma(Hq, Hkv, D, B, dtype)) return PA_ERR_UNSUPPORTED;
+        break;
+    default:
+        return PA_ERR_UNSUPPORTED;
+    }
+    const long long max_ctx = (long long)max_blocks * B;
+    pa_plan p{};
+    *q_blocks = 0;
+    if (kernel == PA_KERNEL_MFMA) {
+        const int qpb = pa::kPrefillColumns / (Hq / Hkv);
+        const long long qb = (max_query_len + qpb - 1) / qpb;
+        const long long groups = qb * S * Hkv;
+        if (groups >= (1LL << 31)) return PA_ERR_SHAPE;
+        long long part;
+        if (req > 0) {
+            part = req;
+        } else if (groups >= kPrefillMinGroups || max_ctx <= 256) {
+            part = max_ctx;                                        // one pass
+        } else {
+            const long long want = (kPrefillMinGroups + groups - 1) / (groups > 0 ? groups : 1);
+            part = (max_ctx + want - 1) / want;
+            part = (part + 127) / 128 * 128;
+            if (part < 256) part = 256;
+        }
+        if (part >= max_ctx) part = ((max_ctx > 0 ? max_ctx : 1) + 31) / 32 * 32;
+        const long long min_part = (max_ctx + pa::kMaxPartitions - 1) / pa::kMaxPartitions;
+        if (part < min_part) part = (min_part + 31) / 32 * 32;
+        const long long cap = B % 4 != 0 ? 1024LL * B : (long long)INT_MAX;
+        if (part > cap) part = cap / 32 * 32;
+        if (part > INT_MAX) part = INT_MAX / 32 * 32;
+        const long long parts = max_ctx > 0 ? (max_ctx + part - 1) / part : 1;
+        if (parts > pa::kMaxPartitions) return PA_ERR_UNSUPPORTED;
+        p.kernel = kernel;
+        p.partition_tokens = (int)part;
+        p.max_partitions = (int)parts;
+        p.split = parts > 1 ? 1 : 0;
+        *q_blocks = (int)qb;
+    } else {
+        p.kernel = PA_KERNEL_GENERIC;
+        p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
+        p.max_partitions = 1;
+        p.split = 0;
+    }
+    if (p.split) {
+        const size_t rows = (size_t)T * Hq * p.max_partitions;
+        p.workspace_bytes = align256(rows * D * sizeof(float)) + 2 * align256(rows * sizeof(float));
+    }
+    *plan = p;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +319,88 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
         case PA_KERNEL_MFMA: err = pa::launch_mfma(a, dtype, out_dtype, hs); break;
         default: return PA_ERR_UNSUPPORTED;
         }
+        if (err != hipSuccess) return PA_ERR_HIP;
+    }
+    if (plan.split && (stages & PA_STAGE_COMBINE)) {
+        err = pa::launch_combine(a, out_dtype, hs);
+        if (err != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
+}
+
+pa_status pa_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
+                          int max_query_len, pa_dtype dtype, pa_dtype out_dtype,
+                          const pa_config *cfg, pa_plan *plan) {
+    if (!plan) return PA_ERR_NULL;
+    int qb;
+    return make_prefill_plan(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype, out_dtype,
+                             cfg, plan, &qb);
+}
+
+pa_status pa_prefill(const void *query, const void *key_cache, const void *value_cache,
+                     const int32_t *block_tables, const int32_t *seq_lens,
+                     const int32_t *query_start, float scale, void *out, int S, int T, int Hq,
+                     int Hkv, int D, int B, int NB, int max_blocks, int max_query_len,
+                     pa_dtype dtype, pa_dtype out_dtype, const pa_config *cfg, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    pa_plan plan;
+    int qb = 0;
+    pa_status st = make_prefill_plan(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype,
+                                     out_dtype, cfg, &plan, &qb);
+    if (st != PA_OK) return st;
+    if (S == 0 || T == 0) return PA_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !seq_lens || !query_start || !out)
+        return PA_ERR_NULL;
+    if (plan.kernel != PA_KERNEL_GENERIC &&
+        !(aligned16(query) && aligned16(key_cache) && aligned16(value_cache) && aligned16(out))) {
+        if (cfg && cfg->kernel != PA_KERNEL_AUTO) return PA_ERR_UNSUPPORTED;
+        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0, 0};
+        st = make_prefill_plan(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype, out_dtype,
+                               &gen, &plan, &qb);
+        if (st != PA_OK) return st;
+    }
+    const int stages = (cfg && cfg->stages) ? cfg->stages : PA_STAGE_ALL;
+
+    Args a;
+    std::memset(&a, 0, sizeof a);
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.S = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.B = B;
+    a.NB = NB;
+    a.max_blocks = max_blocks;
+    a.log2B = is_pow2(B) ? ilog2(B) : -1;
+    a.part_tokens = plan.partition_tokens;
+    a.max_parts = plan.max_partitions;
+    a.split = plan.split;
+    a.stream_kv = (cfg && cfg->kv_reuse) ? 0 : 1;
+    a.query_start = query_start;
+    a.T = T;
+    a.q_blocks = qb;
+    if (plan.split) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+            workspace_bytes < plan.workspace_bytes)
+            return PA_ERR_WORKSPACE;
+        const size_t rows = (size_t)T * Hq * plan.max_partitions;
+        char *ws = static_cast<char *>(workspace);
+        a.part_o = reinterpret_cast<float *>(ws);
+        a.part_m = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)));
+        a.part_l = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)) +
+                                             align256(rows * sizeof(float)));
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t err = hipSuccess;
+    if (stages & PA_STAGE_PARTITIONS) {
+        err = plan.kernel == PA_KERNEL_MFMA ? pa::launch_prefill(a, dtype, out_dtype, hs)
+                                            : pa::launch_generic(a, dtype, out_dtype, hs);
         if (err != hipSuccess) return PA_ERR_HIP;
     }
     if (plan.split && (stages & PA_STAGE_COMBINE)) {

@@ -14,8 +14,12 @@
 // columns 4 (t % 32) .. +3 and partitions t / 32, t / 32 + 8, ..., merged
 // online, so every partial row is read with full-width 16-byte loads and all
 // partitions are in flight at once; the eight group states meet in LDS.
+//
+// Multi-token (causal) calls combine per query row: row r attends lim tokens
+// (pa_rows.h) and has ceil(lim / P) partitions.
 #include "pa_internal.h"
 #include "pa_device.h"
+#include "pa_rows.h"
 
 namespace pa {
 
@@ -29,13 +33,13 @@ constexpr int kGroups = kThreads / kCols;     // partitions handled in parallel
 template <typename OutT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(Args a) {
     const int h = blockIdx.x;
-    const int s = blockIdx.y;
+    const int qrow = blockIdx.y;               // sequence (decode) or query row
     const int t = threadIdx.x;
-    const int L = a.seq_lens[s];
+    const int L = a.query_start ? query_row(a, qrow).lim : a.seq_lens[qrow];
     const int np = (L + a.part_tokens - 1) / a.part_tokens;
     if (np <= 1) return;
 
-    const size_t row = (size_t)s * a.Hq + h;
+    const size_t row = (size_t)qrow * a.Hq + h;
     const float *pm = a.part_m + row * a.max_parts;
     const float *pl = a.part_l + row * a.max_parts;
     const float4 *po = reinterpret_cast<const float4 *>(a.part_o + row * a.max_parts * kD);
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a) {
 
 hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st) {
     if (a.D != kD) return hipErrorInvalidValue;
-    dim3 grid(a.Hq, a.S);
+    dim3 grid(a.Hq, a.query_start ? a.T : a.S);
     switch (odt) {
     case PA_F32: hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(kThreads), 0, st, a); break;
     case PA_F16: hipLaunchKernelGGL(combine_kernel<_Float16>, grid, dim3(kThreads), 0, st, a); break;

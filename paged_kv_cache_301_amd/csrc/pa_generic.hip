@@ -12,8 +12,12 @@
 // straight from its physical slot), the chunk's max / weights update the
 // running state, the weights go to LDS, and lanes then own head dimensions
 // (d = lane + 64 k) to accumulate the weighted value rows.
+//
+// Multi-token (causal) calls run the same kernel over query rows: row r of
+// sequence s attends the first lim tokens of s (pa_rows.h).
 #include "pa_internal.h"
 #include "pa_device.h"
+#include "pa_rows.h"
 
 namespace pa {
 
@@ -22,11 +26,18 @@ constexpr int kGenericMaxD = 512;
 template <typename T, typename OutT>
 __global__ __launch_bounds__(64) void generic_kernel(Args a) {
     const int h = blockIdx.x;
-    const int s = blockIdx.y;
+    const int r = blockIdx.y;                 // query row: sequence (decode) or token
     const int lane = threadIdx.x;
     const int D = a.D, B = a.B;
     const int kvh = h / (a.Hq / a.Hkv);
-    const int L = a.seq_lens[s];
+    int s = r, L;
+    if (a.query_start) {
+        const QueryRow qr = query_row(a, r);
+        s = qr.s;
+        L = qr.lim;
+    } else {
+        L = a.seq_lens[s];
+    }
     const int32_t *table = a.block_tables + (size_t)s * a.max_blocks;
     const size_t head_stride = (size_t)B * D;             // one (block, kv head) tile
     const size_t block_stride = (size_t)a.Hkv * head_stride;
@@ -34,7 +45,7 @@ __global__ __launch_bounds__(64) void generic_kernel(Args a) {
     __shared__ float q_s[kGenericMaxD];
     __shared__ float p_s[64];
     for (int d = lane; d < D; d += 64)
-        q_s[d] = Elem<T>::load(a.query, ((size_t)s * a.Hq + h) * D + d);
+        q_s[d] = Elem<T>::load(a.query, ((size_t)r * a.Hq + h) * D + d);
     __syncthreads();
 
     float o[kGenericMaxD / 64];
@@ -81,13 +92,13 @@ __global__ __launch_bounds__(64) void generic_kernel(Args a) {
 #pragma unroll
     for (int k = 0; k < kGenericMaxD / 64; ++k) {
         const int d = lane + 64 * k;
-        if (d < D) store_elem<OutT>(a.out, ((size_t)s * a.Hq + h) * D + d, o[k] * inv);
+        if (d < D) store_elem<OutT>(a.out, ((size_t)r * a.Hq + h) * D + d, o[k] * inv);
     }
 }
 
 template <typename T, typename OutT>
 static hipError_t launch_generic_t(const Args &a, hipStream_t st) {
-    dim3 grid(a.Hq, a.S);
+    dim3 grid(a.Hq, a.query_start ? a.T : a.S);
     hipLaunchKernelGGL((generic_kernel<T, OutT>), grid, dim3(64), 0, st, a);
     return hipGetLastError();
 }

@@ -29,6 +29,10 @@ struct Args {
     int split;                // 1: write partials, 0: write final output
     int stream_kv;            // 1: K / V loads carry the non-temporal hint
     int compact;              // 1: 1-D grid decoded into live items (pa_sched.h)
+    // Multi-token (causal) calls only; query_start is null for decode.
+    const int32_t *query_start;   // [S+1] rows query_start[s] .. query_start[s+1]-1 are sequence s's
+    int T;                        // query rows; query / out are [T][Hq][D]
+    int q_blocks;                 // query blocks per sequence in the grid
 };
 
 // Launchers return hipErrorInvalidValue when no instantiation covers the
@@ -37,6 +41,11 @@ hipError_t launch_generic(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t 
 hipError_t launch_valu(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
 hipError_t launch_mfma(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
 hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st);
+hipError_t launch_prefill(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
+
+// Query tokens per work-group of the multi-token matrix-core kernel: its four
+// waves hold 64 (query token, head) columns.
+constexpr int kPrefillColumns = 64;
 hipError_t launch_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
                            const int32_t *block_tables, const int32_t *seq_lens,
                            void *key_cache, void *value_cache, int T, int Hkv, int D, int B,

@@ -80,6 +80,11 @@ SPECS = {
                              dtype="bf16", lens=("uniform", 16384, 32768),
                              max_len=32768, pool=("free", 0.25), seed=5,
                              prefix_tokens=4096),
+    # chunked prefill: 16 seqs, 32 q / 8 kv heads, D=128, B=16, bf16, contexts
+    # L ~ U[1024, 8192] of which the last 512 tokens are new (the chunk).
+    "prefill": WorkloadSpec("prefill", S=16, Hq=32, Hkv=8, D=128, B=16, dtype="bf16",
+                            lens=("uniform", 1024, 8192), max_len=8192, pool=("free", 0.25),
+                            seed=7),
     # multi-query: 256 seqs, 64 q heads on one kv head, D=128, B=16, bf16,
     # L ~ U[512, 4096], pool = need + 25 %.
     "mqa": WorkloadSpec("mqa", S=256, Hq=64, Hkv=1, D=128, B=16, dtype="bf16",
@@ -267,3 +272,56 @@ def make_workload(name_or_spec, *, device="cpu", poison: bool = False,
         seq_lens=torch.as_tensor(lens.astype(np.int32)).to(dev),
         scale=scale, NB=NB, max_blocks=max_blocks, lens=lens,
         refcount=refcount, poison_block=poison_block, tables_host=tables)
+
+
+# New tokens per sequence of the multi-token (causal) workloads.
+PREFILL_NEW = {"prefill": 512}
+
+
+@dataclass
+class PrefillWorkload:
+    """A decode workload plus the new tokens' query rows of a causal call:
+    sequence s owns rows query_start[s] .. query_start[s+1]-1, its last n_s
+    tokens (already in the cache)."""
+    base: Workload
+    query: torch.Tensor          # [T, Hq, D]
+    query_start: torch.Tensor    # [S+1] int32
+    n_new: np.ndarray            # [S] int64
+    max_query_len: int
+
+    @property
+    def T(self) -> int:
+        return int(self.n_new.sum())
+
+    def flops(self) -> int:
+        """Algorithmic flops: 4 D per (query row, head, attended token)."""
+        total = 0
+        for L, n in zip(self.base.lens.tolist(), self.n_new.tolist()):
+            # rows attend L-n+1 .. L tokens
+            total += n * (L - n) + n * (n + 1) // 2
+        return 4 * self.base.D * self.base.Hq * total
+
+
+def make_prefill_workload(name_or_spec, n_new=None, *, device="cpu", poison: bool = False,
+                          **overrides) -> PrefillWorkload:
+    """The named workload with n_new new tokens per sequence (an int, capped
+    at each length, or one count per sequence); query rows are N(0,1) draws
+    from a generator seeded with the spec's seed + 1."""
+    w = make_workload(name_or_spec, device=device, poison=poison, **overrides)
+    if n_new is None:
+        n_new = PREFILL_NEW[w.spec.name]
+    if isinstance(n_new, (int, np.integer)):
+        n = np.minimum(w.lens, int(n_new)).astype(np.int64)
+    else:
+        n = np.asarray(n_new, dtype=np.int64)
+        if n.shape != w.lens.shape or (n > w.lens).any() or (n < 0).any():
+            raise ValueError("n_new must give 0 <= n_s <= L_s per sequence")
+    qs = np.zeros(w.S + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(n)
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.spec.seed + 1)
+    q = torch.empty((int(n.sum()), w.Hq, w.D), dtype=w.dtype, device=dev)
+    _normal_fill(q, gen)
+    return PrefillWorkload(base=w, query=q, query_start=torch.as_tensor(qs).to(dev), n_new=n,
+                           max_query_len=int(n.max(initial=0)))

@@ -34,7 +34,12 @@ MUTANTS = {
                            "for (int tt = 0; tt < n - 1; ++tt)\n        for (int d = 0; d < D; ++d) o[d]"),
     "half_bias": ("e - 25", "e - 24"),
     "bf16_shift": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
-    "query_index": ("((size_t)s * Hq + h) * D + d", "((size_t)h * 1 + s) * D + d"),
+    "query_index": ("((size_t)qrow * Hq + h) * D + d", "((size_t)h * 1 + qrow) * D + d"),
+    "prefill_excludes_self": ("t, pos + 1, scale, out", "t, pos, scale, out"),
+    "prefill_no_offset": ("int pos = seq_lens[s] - n + (t - query_start[s]);",
+                          "int pos = t - query_start[s];"),
+    "prefill_sequence_row": ("t, pos + 1, scale, out", "s, pos + 1, scale, out"),
+    "prefill_future_visible": ("t, pos + 1, scale, out", "t, seq_lens[s], scale, out"),
     "score_sign": ("acc += qv[d] * K", "acc -= qv[d] * K"),
 }
 
@@ -79,6 +84,22 @@ def _battery():
         ref = sdpa_reference(qq, Ks, Vs, 0.4).numpy()
         if not np.max(np.abs(got - ref)) < 1e-12:
             failed.append(f"sdpa_{dtype}")
+    # several new tokens per sequence against masked unpaged attention
+    from test_prefill import causal_reference
+    gen = torch.Generator().manual_seed(6)
+    lens, n_new = [1, 9, 14, 6], [1, 4, 14, 2]
+    Ks, Vs = random_logical(4, 2, 6, lens, gen=gen)
+    qq = torch.randn((sum(n_new), 4, 6), generator=gen)
+    pk = scatter_paged(Ks, Vs, 4, rng=np.random.default_rng(6))
+    qs = torch.tensor(np.concatenate([[0], np.cumsum(n_new)]), dtype=torch.int32)
+    try:
+        got = oracle.prefill(qq, pk["key_cache"], pk["value_cache"], pk["block_tables"],
+                             pk["seq_lens"], qs, 0.4)
+        ref = causal_reference(qq, Ks, Vs, n_new, 0.4).numpy()
+        if not np.max(np.abs(got - ref)) < 1e-12:
+            failed.append("prefill_sdpa")
+    except ValueError:
+        failed.append("prefill_raised")
     # large scores
     L = 9
     K = torch.zeros((L, 1, 2))
