@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--print-source-sha", action="store_true",
-                    help="print the kernel-source hash used to match counter records, then exit")
+                    help="print each kernel's source hash (used to match counter records), then exit")
     ap.add_argument("--op", choices=["decode", "write_kv", "append_kv", "copy_blocks", "prefill"],
                     default="decode",
                     help="decode (default): the attention step; write_kv: store a prompt chunk's "
@@ -65,15 +65,30 @@ def parse():
     return ap.parse_args()
 
 
-def source_sha256() -> str:
-    """Hash of the kernel sources (ties hardware-counter records to a build)."""
-    import glob
+# Sources each kernel is built from: a traffic record stays valid while these
+# files are unchanged.
+_COMMON = ["pa_device.h", "pa_internal.h"]
+KERNEL_SOURCES = {
+    "pa_valu_partitions": ["pa_valu.hip", "pa_tile.h", "pa_table.h", "pa_sched.h"] + _COMMON,
+    "pa_mfma_partitions": ["pa_mfma.hip", "pa_mfma_core.h", "pa_tile.h", "pa_table.h",
+                           "pa_sched.h"] + _COMMON,
+    "pa_generic_partitions": ["pa_generic.hip", "pa_rows.h"] + _COMMON,
+    "pa_prefill_mfma": ["pa_prefill.hip", "pa_mfma_core.h", "pa_tile.h", "pa_table.h",
+                        "pa_rows.h"] + _COMMON,
+    "pa_prefill_generic": ["pa_generic.hip", "pa_rows.h"] + _COMMON,
+    "pa_kv_write": ["pa_kvwrite.hip"] + _COMMON,
+    "pa_copy_blocks": ["pa_kvwrite.hip"] + _COMMON,
+}
+
+
+def source_sha256(kernel: str) -> str:
+    """Hash of one kernel's source files (ties hardware-counter records to a build)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_301_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    for name in sorted(KERNEL_SOURCES[kernel]):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -82,7 +97,9 @@ def recorded_traffic(kernel: str, workload: str, block_size: int):
     if one was recorded for these exact kernel sources; else None."""
     import glob
     import re
-    sha = source_sha256()
+    if kernel not in KERNEL_SOURCES:
+        return None
+    sha = source_sha256(kernel)
     pat = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) "
                      r"source_sha256=([0-9a-f]+) read_bytes=(\d+) write_bytes=(\d+)")
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -362,7 +379,7 @@ def bench_prefill(args, dev):
 def main():
     args = parse()
     if args.print_source_sha:
-        print(source_sha256())
+        print(json.dumps({k: source_sha256(k) for k in KERNEL_SOURCES}))
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -379,6 +396,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.op == "prefill":
         bench_prefill(args, dev)
         return
@@ -395,14 +420,6 @@ def main():
           f"kv={w.kv_bytes() / 1e9:.3f} GB (generated in {time.perf_counter() - t_gen:.1f}s)",
           file=sys.stderr, flush=True)
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     if args.op != "decode":
         bench_write(args, w, dev)
         return

@@ -195,7 +195,7 @@ pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB,
         const int qpb = pa::kPrefillColumns / (Hq / Hkv);
         const long long qb = (max_query_len + qpb - 1) / qpb;
         const long long groups = qb * S * Hkv;
-        if (groups >= (1LL << 31)) return PA_ERR_SHAPE;
+        if ((groups + 8 * qb) >= (1LL << 31)) return PA_ERR_SHAPE;   // grid x, padded to whole XCD rounds
         long long part;
         if (req > 0) {
             part = req;

@@ -113,50 +113,69 @@ __device__ __forceinline__ void mfma_stage(const KVTile &tile, uint4 *klds, uint
     }
 }
 
-// Scores, online softmax update and P.V for one staged 32-token sub-tile
-// starting at token t0.  Token t counts for this lane's column iff t < lim;
-// t_full (wave-uniform, <= every column's lim) marks sub-tiles that need no
-// mask.  Decode: lim = t_full = the partition end, and t0 < lim.  With
-// PER_COLUMN, a column may have seen no valid token yet (its running max is
-// still -inf) and its weights are then forced to 0.
-template <typename T, bool PER_COLUMN = false>
-__device__ __forceinline__ void mfma_subtile(MfmaState<T> &st, const typename Mfma<T>::Vec (&qf)[4],
-                                             const uint4 *klds, const uint4 *vlds, int t0,
-                                             int lim, int t_full, int g, int i, float scale_log2) {
+// Scores, online softmax update and P.V for NS staged 32-token sub-tiles
+// (LDS images klds[u] / vlds[u]) starting at tokens t0 + 32 u, of which the
+// first nsub (wave-uniform, 1 <= nsub <= NS) are inside the partition.  All
+// score products are issued before the softmax and all P.V products after
+// it, so the matrix core has independent work while the vector unit waits,
+// and one maximum / rescale step serves all NS sub-tiles.  Token t counts for
+// this lane's column iff t < lim; t_full (wave-uniform, <= every column's
+// lim) marks sub-tiles that need no mask.  Decode: lim = t_full = the
+// partition end, and t0 < lim.  With PER_COLUMN, a column may have seen no
+// valid token yet (its running max is still -inf) and its weights are then
+// forced to 0.
+template <typename T, int NS, bool PER_COLUMN = false>
+__device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma<T>::Vec (&qf)[4],
+                                           const uint4 (*klds)[32 * 16], const uint4 (*vlds)[32 * 16],
+                                           int t0, int nsub, int lim, int t_full, int g, int i,
+                                           float scale_log2) {
     using M = Mfma<T>;
     using Vec = typename M::Vec;
-    // scores: A operand = chunk 4kk + g of row 16u + i (swizzle swz_k = i)
-    f32x4 acc[2];
+    // scores: A operand = chunk 4kk + g of row 16h + i (swizzle swz_k = i)
+    f32x4 acc[NS][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NS; ++u) {
+        if (u >= nsub) break;                        // uniform
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const uint4 a = klds[(16 * u + i) * 16 + ((4 * kk + g) ^ i)];
-            acc[u] = M::mma(bitcast<Vec>(a), qf[kk], acc[u]);
+        for (int h = 0; h < 2; ++h) {
+            acc[u][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint4 a = klds[u][(16 * h + i) * 16 + ((4 * kk + g) ^ i)];
+                acc[u][h] = M::mma(bitcast<Vec>(a), qf[kk], acc[u][h]);
+            }
         }
     }
-    float x[8];
-    if (t0 + 32 <= t_full) {   // uniform: the whole sub-tile counts for every column
+    float x[NS][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = acc[j >> 2][j & 3] * scale_log2;
-    } else {
+    for (int u = 0; u < NS; ++u) {
+        const int tu = t0 + 32 * u;
+        if (u >= nsub) {                              // uniform: past the partition
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            x[j] = (t0 + 16 * (j >> 2) + 4 * g + (j & 3) < lim) ? acc[j >> 2][j & 3] * scale_log2
-                                                                : kNegInf;
+            for (int j = 0; j < 8; ++j) x[u][j] = kNegInf;
+        } else if (tu + 32 <= t_full) {               // uniform: counts for every column
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[u][j] = acc[u][j >> 2][j & 3] * scale_log2;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                x[u][j] = (tu + 16 * (j >> 2) + 4 * g + (j & 3) < lim)
+                              ? acc[u][j >> 2][j & 3] * scale_log2 : kNegInf;
+        }
     }
-    float mt = x[0];
+    float mt = x[0][0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, x[j]);
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mt = fmaxf(mt, x[u][j]);
     mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
-    // The reference point st.m moves only when a head's maximum exceeds it by
-    // more than kRescaleSlack (log2 units; always on the first sub-tile, where
-    // st.m = -inf): otherwise the weights are taken against the stale value
-    // (p <= 2^kRescaleSlack, exact in fp32) and the rescale of O, which is most
-    // of a sub-tile's vector work, is skipped for the whole wave.  o / l and
-    // the partial triple (m, l, o) are the same quantities either way.
+    // The reference point st.m moves only when a column's maximum exceeds it
+    // by more than kRescaleSlack (log2 units; always on the first sub-tile,
+    // where st.m = -inf): otherwise the weights are taken against the stale
+    // value (p <= 2^kRescaleSlack, exact in fp32) and the rescale of O, which
+    // is most of a sub-tile's vector work, is skipped for the whole wave.
+    // o / l and the partial triple (m, l, o) are the same quantities either way.
     const bool grow = mt > st.m + kRescaleSlack;     // false while mt = -inf
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {    // uniform branch
         const float mn = grow ? mt : st.m;
@@ -170,33 +189,38 @@ __device__ __forceinline__ void mfma_subtile(MfmaState<T> &st, const typename Mf
     }
     // a column with no valid token so far keeps m = -inf: its weights are 0
     const float mref = (PER_COLUMN && st.m == kNegInf) ? 0.f : st.m;
-    float p[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(x[j] - mref);
-        ps += p[j];
-    }
-    st.l += ps;
-    Vec phi, plo;
-    split_probs<T>(p, phi, plo);
 
     const int row_a = 4 * g + (i >> 2);
     const int sw = swz_v(row_a);
     const int lane_off = row_a * kRowBytes + ((i & 3) << 3);
+    float ps = 0.f;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-        const int off = lane_off + (((2 * n) ^ sw) << 4);
-        struct { i16x4 a, b; } raw = {lds_read_tr16(vlds, off), lds_read_tr16(vlds, off + 16 * kRowBytes)};
-        const Vec va = bitcast<Vec>(raw);
-        st.o[n] = M::mma(va, phi, st.o[n]);
-        st.o[n] = M::mma(va, plo, st.o[n]);
+    for (int u = 0; u < NS; ++u) {
+        if (u >= nsub) break;                        // uniform
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(x[u][j] - mref);
+            ps += p[j];
+        }
+        Vec phi, plo;
+        split_probs<T>(p, phi, plo);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            const int off = lane_off + (((2 * n) ^ sw) << 4);
+            struct { i16x4 a, b; } raw = {lds_read_tr16(vlds[u], off),
+                                          lds_read_tr16(vlds[u], off + 16 * kRowBytes)};
+            const Vec va = bitcast<Vec>(raw);
+            st.o[n] = M::mma(va, phi, st.o[n]);
+            st.o[n] = M::mma(va, plo, st.o[n]);
+        }
     }
+    st.l += ps;
 }
 
-// One iteration: every wave stages its sub-tile, then runs all W sub-tiles
-// that start before t_end (the partition end).  t0 = first token of the
-// iteration; lim / t_full as in mfma_subtile.
+// One iteration: every wave stages its sub-tile, then all W sub-tiles that
+// start before t_end (the partition end) are consumed together.  t0 = first
+// token of the iteration; lim / t_full as in mfma_tiles.
 template <typename T, int W, bool PER_COLUMN = false>
 __device__ __forceinline__ void mfma_compute(MfmaState<T> &st, const KVTile &tile,
                                              const typename Mfma<T>::Vec (&qf)[4],
@@ -205,12 +229,8 @@ __device__ __forceinline__ void mfma_compute(MfmaState<T> &st, const KVTile &til
                                              int g, int i, float scale_log2) {
     mfma_stage(tile, klds[w], vlds[w], g, i);
     __syncthreads();   // rows visible to every lane of every wave
-#pragma unroll
-    for (int u = 0; u < W; ++u) {
-        if (t0 + 32 * u >= t_end) break;   // uniform: the rest of the iteration is past the end
-        mfma_subtile<T, PER_COLUMN>(st, qf, klds[u], vlds[u], t0 + 32 * u, lim, t_full, g, i,
-                                    scale_log2);
-    }
+    const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
+    mfma_tiles<T, W, PER_COLUMN>(st, qf, klds, vlds, t0, nsub, lim, t_full, g, i, scale_log2);
     __syncthreads();   // reads done before the next iteration overwrites LDS
 }
 

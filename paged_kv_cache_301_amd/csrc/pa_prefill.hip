@@ -35,6 +35,7 @@ namespace {
 using namespace mfma;
 
 constexpr int kWaves = kPrefillColumns / 16;
+constexpr int kXcds = 8;   // accelerator dies: consecutive work-group ids alternate between them
 
 template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
 __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(Args a) {
@@ -42,11 +43,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(Args a) {
     constexpr int QPB = kPrefillColumns / G;     // query tokens per work-group
     static_assert(QPB * G == kPrefillColumns, "G divides the column count");
 
-    // x = (query block, sequence, kv head), kv head fastest; y = partition
-    const int kvh = blockIdx.x % a.Hkv;
-    const int rest = blockIdx.x / a.Hkv;
-    const int s = rest % a.S;
-    const int qb = rest / a.S;
+    // x: work-groups are dealt round-robin to the 8 XCDs (x mod 8); the
+    // query blocks of one (sequence, kv head) pair get consecutive slots of
+    // one XCD, so they start together and stream the same K / V tiles through
+    // that XCD's L2 instead of each reading them from HBM.  y = partition.
+    const int xcd = blockIdx.x % kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int qb = slot % a.q_blocks;
+    const int pair = (slot / a.q_blocks) * kXcds + xcd;
+    if (pair >= a.S * a.Hkv) return;
+    const int s = pair / a.Hkv;
+    const int kvh = pair % a.Hkv;
     const int p = blockIdx.y;
 
     const int qs = a.query_start[s];
@@ -162,7 +169,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(Args a) {
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    const dim3 grid((unsigned)((long long)a.q_blocks * a.S * a.Hkv), a.max_parts);
+    const long long pairs = (long long)a.S * a.Hkv;
+    const dim3 grid((unsigned)((pairs + kXcds - 1) / kXcds * kXcds * a.q_blocks), a.max_parts);
     const dim3 block(64 * kWaves);
     const bool scalar = a.B % 4 == 0;
     if (a.stream_kv) {
