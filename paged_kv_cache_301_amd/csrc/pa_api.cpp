@@ -161,8 +161,8 @@ bool supports_prefill_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
 }
 
 // Work-groups below which the automatic plan splits contexts: the grid then
-// holds fewer than two four-wave groups per CU.
-constexpr long long kPrefillMinGroups = 1024;
+// holds fewer than one round of four-wave groups (two per CU).
+constexpr long long kPrefillMinGroups = 512;
 
 pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
                             int max_query_len, pa_dtype dtype, pa_dtype out_dtype,

@@ -43,9 +43,9 @@ hipError_t launch_mfma(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st)
 hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st);
 hipError_t launch_prefill(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
 
-// Query tokens per work-group of the multi-token matrix-core kernel: its four
-// waves hold 64 (query token, head) columns.
-constexpr int kPrefillColumns = 64;
+// (query token, head) columns per work-group of the multi-token matrix-core
+// kernel: four waves of four 16-column groups.
+constexpr int kPrefillColumns = 128;
 hipError_t launch_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
                            const int32_t *block_tables, const int32_t *seq_lens,
                            void *key_cache, void *value_cache, int T, int Hkv, int D, int B,

@@ -10,17 +10,24 @@
 //     S^T [tokens x (query, head)] = K . Q^T,   O^T += V^T . P^T
 //
 // One work-group of four waves handles one (sequence, kv head, block of
-// query tokens, context partition).  Its 64 columns are (query token, head)
+// query tokens, context partition).  Its 128 columns are (query token, head)
 // pairs, column c = token c / G, head c % G of the kv head's group, so a block
-// holds 64 / G query tokens (64 for G = 1, 1 for G = 64) and wave w owns
-// columns 16 w .. 16 w + 15.  An iteration covers 128 tokens: each wave loads
-// one 32-token sub-tile of whole K / V rows (pa_tile.h), stages it in LDS,
-// and every wave runs the two products for its columns over the four
-// sub-tiles (pa_mfma_core.h).  Each column masks the tokens past its own
+// holds 128 / G query tokens; wave w owns columns 32 w .. 32 w + 31 as two
+// groups of 16 (the matrix core's column width).  An iteration covers one
+// 32-token sub-tile of whole K / V rows (pa_tile.h): each wave loads a quarter
+// of its rows, the four quarters meet in a double-buffered LDS image (one
+// barrier per iteration), and every wave reads the K and V^T fragments of the
+// sub-tile once and runs the two products for both of its column groups
+// with them -- twice the matrix-core work per LDS byte and per fragment read
+// of a one-group wave.  Each column masks the tokens past its own
 // position; sub-tiles below the block's first query position need no mask.
 // The context loop of a block stops at its last query's position, so early
 // query blocks read a shorter context.  Long contexts are cut into
 // partitions merged by the same log-sum-exp combine as decode, per query row.
+// Measured on MI355X (chunked-prefill workload): four groups per wave (O in
+// the accumulation registers, one wave per SIMD) ran at 404 TFLOP/s, one
+// group per wave with four sub-tiles per iteration at 440, two groups per
+// wave at two waves per SIMD at 529.
 #include "pa_internal.h"
 #include "pa_device.h"
 #include "pa_table.h"
@@ -34,11 +41,107 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = kPrefillColumns / 16;
+constexpr int kWaves = 4;
+constexpr int kGroups = kPrefillColumns / (16 * kWaves);   // 16-column groups per wave
+static_assert(16 * kGroups * kWaves == kPrefillColumns, "columns per work-group");
+constexpr int kLoads = kTileLoads / kWaves;         // load instructions per operand per wave
 constexpr int kXcds = 8;   // accelerator dies: consecutive work-group ids alternate between them
 
+// This wave's quarter of a sub-tile (rows 4 (k0 + k) + g, chunk i) to the
+// swizzled LDS images.
+__device__ __forceinline__ void stage_quarter(const KVTileN<kLoads> &tile, uint4 *klds, uint4 *vlds,
+                                              int k0, int g, int i) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int row = 4 * (k0 + k) + g;
+        klds[row * 16 + (i ^ swz_k(row))] = tile.k[k];
+        vlds[row * 16 + (i ^ swz_v(row))] = tile.v[k];
+    }
+}
+
+// One staged 32-token sub-tile starting at t0 for the wave's column
+// groups.  lim[j]: tokens column group j's lane may see; t_full: uniform
+// bound below which no column masks.
+template <typename T>
+__device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
+                                               const typename Mfma<T>::Vec (&qf)[kGroups][4],
+                                               const uint4 *klds, const uint4 *vlds, int t0,
+                                               const int (&lim)[kGroups], int t_full, int g, int i,
+                                               float scale_log2) {
+    using M = Mfma<T>;
+    using Vec = typename M::Vec;
+    // K fragments: A operand = chunk 4kk + g of row 16h + i (swizzle swz_k = i)
+    Vec kf[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kf[h][kk] = bitcast<Vec>(klds[(16 * h + i) * 16 + ((4 * kk + g) ^ i)]);
+    f32x4 acc[kGroups][2];
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            acc[j][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc[j][h] = M::mma(kf[h][kk], qf[j][kk], acc[j][h]);
+        }
+    // V^T fragments (see swz_v): the same for every group
+    const int row_a = 4 * g + (i >> 2);
+    const int sw = swz_v(row_a);
+    const int lane_off = row_a * kRowBytes + ((i & 3) << 3);
+    Vec vf[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        const int off = lane_off + (((2 * n) ^ sw) << 4);
+        struct { i16x4 a, b; } raw = {lds_read_tr16(vlds, off), lds_read_tr16(vlds, off + 16 * kRowBytes)};
+        vf[n] = bitcast<Vec>(raw);
+    }
+    const bool full = t0 + 32 <= t_full;          // uniform
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = acc[j][e >> 2][e & 3] * scale_log2;
+            x[e] = (full || t0 + 16 * (e >> 2) + 4 * g + (e & 3) < lim[j]) ? v : kNegInf;
+        }
+        float mt = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+        mt = fmaxf(mt, shfl_xor(mt, 16));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        // deferred rescale, as in mfma_tiles
+        const bool grow = mt > st[j].m + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float mn = grow ? mt : st[j].m;
+            const float alpha = grow ? fast_exp2(st[j].m - mn) : 1.f;
+            st[j].l *= alpha;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) st[j].o[n] *= alpha;
+            st[j].m = mn;
+        }
+        const float mref = st[j].m == kNegInf ? 0.f : st[j].m;
+        float p[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = fast_exp2(x[e] - mref);
+            ps += p[e];
+        }
+        st[j].l += ps;
+        Vec phi, plo;
+        split_probs<T>(p, phi, plo);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            st[j].o[n] = M::mma(vf[n], phi, st[j].o[n]);
+            st[j].o[n] = M::mma(vf[n], plo, st[j].o[n]);
+        }
+    }
+}
+
 template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
-__global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(Args a) {
+__global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
     constexpr int QPB = kPrefillColumns / G;     // query tokens per work-group
     static_assert(QPB * G == kPrefillColumns, "G divides the column count");
@@ -68,39 +171,48 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(Args a) {
     const int t_begin = p * a.part_tokens;
     if (t_begin >= lim_max) return;              // uniform: nothing of this partition is visible
     const int t_end = min(lim_max, t_begin + a.part_tokens);
+    const int t_full = min(lim_min, t_end);      // below this every column sees every token
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15;
     const int g = lane >> 4;
-    const int c = 16 * w + i;                    // column: (query token c / G, head c % G)
-    const int qi = c / G;
-    const int hg = c % G;
-    const bool col_ok = q_first + qi <= q_last;
-    const int lim = col_ok ? base + q_first + qi + 1 : 0;   // this column's visible tokens
-    const int lim_eff = min(lim, t_end);
-    const int t_full = min(lim_min, t_end);      // below this every column sees every token
-    const int row = qs + q_first + qi;           // query row
-    const int head = kvh * G + hg;
 
-    __shared__ uint4 klds[kWaves][32 * 16];
-    __shared__ uint4 vlds[kWaves][32 * 16];
-    __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
-
-    Vec qf[4];
-    const T *qrow = static_cast<const T *>(a.query) + ((size_t)(col_ok ? row : qs) * a.Hq + head) * kHeadDim;
+    // the wave's column groups: column c = token c / G, head c % G
+    int lim[kGroups], lim_eff[kGroups], rows[kGroups], heads[kGroups];
+    bool ok[kGroups];
+    Vec qf[kGroups][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        uint4 v = *reinterpret_cast<const uint4 *>(qrow + 8 * g + 32 * kk);
-        if (!col_ok) v = make_uint4(0, 0, 0, 0);
-        qf[kk] = bitcast<Vec>(v);
+    for (int j = 0; j < kGroups; ++j) {
+        const int c = 16 * kGroups * w + 16 * j + i;
+        const int qi = c / G;
+        ok[j] = q_first + qi <= q_last;
+        lim[j] = ok[j] ? base + q_first + qi + 1 : 0;
+        lim_eff[j] = min(lim[j], t_end);
+        rows[j] = qs + q_first + qi;
+        heads[j] = kvh * G + c % G;
+        const T *qrow = static_cast<const T *>(a.query) +
+                        ((size_t)(ok[j] ? rows[j] : qs) * a.Hq + heads[j]) * kHeadDim;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            uint4 v = *reinterpret_cast<const uint4 *>(qrow + 8 * g + 32 * kk);
+            if (!ok[j]) v = make_uint4(0, 0, 0, 0);
+            qf[j][kk] = bitcast<Vec>(v);
+        }
     }
 
-    MfmaState<T> st;
+    MfmaState<T> st[kGroups];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) st.o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m = kNegInf;
-    st.l = 0.f;
+    for (int j = 0; j < kGroups; ++j) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) st[j].o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[j].m = kNegInf;
+        st[j].l = 0.f;
+    }
+
+    __shared__ uint4 klds[2][32 * 16];
+    __shared__ uint4 vlds[2][32 * 16];
+    __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
 
     TileLoader<SCALAR, STREAM> ctx;
     const size_t head_bytes = (size_t)a.B * kRowBytes;
@@ -119,50 +231,58 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(Args a) {
         __syncthreads();
     }
 
-    constexpr int kIter = 32 * kWaves;
-    const int niter = (t_end - t_begin + kIter - 1) / kIter;
-    const int tw = t_begin + 32 * w;
-    KVTile ta, tb;
-    ctx.load(ta, tw);
+    // One barrier per sub-tile: a wave writes LDS image b only after the
+    // barrier of the previous sub-tile, which every wave reaches after it
+    // has finished reading image b (two sub-tiles earlier).
+    const int niter = (t_end - t_begin + 31) >> 5;
+    const int k0 = kLoads * w;
+    KVTileN<kLoads> ra, rb;
+    ctx.load(ra, t_begin, k0);
     for (int it = 0; it < niter; it += 2) {
-        const int t0 = t_begin + kIter * it;
-        ctx.load(tb, tw + kIter * (it + 1));
+        const int t0 = t_begin + 32 * it;
+        ctx.load(rb, t0 + 32, k0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_compute<T, kWaves, true>(st, ta, qf, klds, vlds, w, t0, t_end, lim_eff, t_full, g, i,
-                                      a.scale_log2);
+        stage_quarter(ra, klds[0], vlds[0], k0, g, i);
+        __syncthreads();
+        subtile_groups<T>(st, qf, klds[0], vlds[0], t0, lim_eff, t_full, g, i, a.scale_log2);
         __builtin_amdgcn_sched_barrier(0);
-        ctx.load(ta, tw + kIter * (it + 2));
+        ctx.load(ra, t0 + 64, k0);
         __builtin_amdgcn_sched_barrier(0);
-        if (it + 1 < niter)
-            mfma_compute<T, kWaves, true>(st, tb, qf, klds, vlds, w, t0 + kIter, t_end, lim_eff,
-                                          t_full, g, i, a.scale_log2);
+        if (it + 1 < niter) {
+            stage_quarter(rb, klds[1], vlds[1], k0, g, i);
+            __syncthreads();
+            subtile_groups<T>(st, qf, klds[1], vlds[1], t0 + 32, lim_eff, t_full, g, i, a.scale_log2);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
-    st.l += shfl_xor(st.l, 16);
-    st.l += shfl_xor(st.l, 32);
 
-    if (!col_ok) return;
-    const int np_row = (lim + a.part_tokens - 1) / a.part_tokens;
-    if (p >= np_row) return;                     // none of this column's tokens are here
-    if (np_row == 1) {
-        const float inv = 1.f / st.l;            // l > 0: token 0 is visible to every row
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+    for (int j = 0; j < kGroups; ++j) {
+        float l = st[j].l;
+        l += shfl_xor(l, 16);
+        l += shfl_xor(l, 32);
+        if (!ok[j]) continue;
+        const int np_row = (lim[j] + a.part_tokens - 1) / a.part_tokens;
+        if (p >= np_row) continue;               // none of this column's tokens are here
+        if (np_row == 1) {
+            const float inv = 1.f / l;           // l > 0: token 0 is visible to every row
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                store_elem<OutT>(a.out, ((size_t)row * a.Hq + head) * kHeadDim + 16 * k + 4 * g + r,
-                                 st.o[k][r] * inv);
-        }
-    } else {
-        const size_t idx = ((size_t)row * a.Hq + head) * a.max_parts + p;
-        float *dst = a.part_o + idx * kHeadDim;
+            for (int k = 0; k < 8; ++k)
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            *reinterpret_cast<float4 *>(dst + 16 * k + 4 * g) =
-                make_float4(st.o[k][0], st.o[k][1], st.o[k][2], st.o[k][3]);
-        if (g == 0) {
-            a.part_m[idx] = st.m;
-            a.part_l[idx] = st.l;
+                for (int r = 0; r < 4; ++r)
+                    store_elem<OutT>(a.out, ((size_t)rows[j] * a.Hq + heads[j]) * kHeadDim + 16 * k + 4 * g + r,
+                                     st[j].o[k][r] * inv);
+        } else {
+            const size_t idx = ((size_t)rows[j] * a.Hq + heads[j]) * a.max_parts + p;
+            float *dst = a.part_o + idx * kHeadDim;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                *reinterpret_cast<float4 *>(dst + 16 * k + 4 * g) =
+                    make_float4(st[j].o[k][0], st[j].o[k][1], st[j].o[k][2], st[j].o[k][3]);
+            if (g == 0) {
+                a.part_m[idx] = st[j].m;
+                a.part_l[idx] = l;
+            }
         }
     }
 }
