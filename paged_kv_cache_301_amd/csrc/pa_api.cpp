@@ -27,12 +27,17 @@ constexpr long long kAutoMinItems = 4096;
 constexpr long long kAutoSinglePass = 256;
 
 // waves: waves per work-group (the matrix-core kernel runs ceil(G / 16)).
+// Wide groups start from twice the minimum: a partition leaves G * D * 4
+// bytes of partial results, 12.5 % of its K / V bytes at G = 64 and 512
+// tokens (measured: 1024-token partitions were 9-10 % faster for G = 32, 64).
 long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
     if (max_ctx <= kAutoSinglePass) return max_ctx;
-    long long part = kAutoPartitionMin;
+    long long part = waves > 1 ? 2 * kAutoPartitionMin : kAutoPartitionMin;
     while (part * kAutoMaxParts < max_ctx) part *= 2;
+    // wide groups settle for one round of wave slots before cutting finer
+    const long long min_waves = waves > 1 ? kAutoMinItems / 2 : kAutoMinItems;
     while (part > kAutoPartitionFloor &&
-           (long long)S * Hkv * waves * ((max_ctx + part - 1) / part) < kAutoMinItems)
+           (long long)S * Hkv * waves * ((max_ctx + part - 1) / part) < min_waves)
         part /= 2;
     return part;
 }
