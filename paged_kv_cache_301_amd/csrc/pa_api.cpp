@@ -20,19 +20,19 @@ using pa::Args;
 // halved (down to kAutoPartitionFloor) while the grid would hold fewer than
 // kAutoMinItems waves over (sequence, kv head, partition) items, so small batches still
 // occupy 256 CUs.  Contexts of at most kAutoSinglePass tokens run in one pass.
-constexpr long long kAutoPartitionMin = 512;
+constexpr long long kAutoPartitionMin = 1024;
 constexpr long long kAutoMaxParts = 32;
 constexpr long long kAutoPartitionFloor = 64;
 constexpr long long kAutoMinItems = 4096;
 constexpr long long kAutoSinglePass = 256;
 
 // waves: waves per work-group (the matrix-core kernel runs ceil(G / 16)).
-// Wide groups start from twice the minimum: a partition leaves G * D * 4
-// bytes of partial results, 12.5 % of its K / V bytes at G = 64 and 512
-// tokens (measured: 1024-token partitions were 9-10 % faster for G = 32, 64).
+// Measured with the longest-first item order: 1024-token partitions beat 512
+// by 2 % (mha_7b), 5 % (gqa_70b) and 8 % (multi-query, whose partial results
+// are G * D * 4 bytes per partition) and tie on gqa_long.
 long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
     if (max_ctx <= kAutoSinglePass) return max_ctx;
-    long long part = waves > 1 ? 2 * kAutoPartitionMin : kAutoPartitionMin;
+    long long part = kAutoPartitionMin;
     while (part * kAutoMaxParts < max_ctx) part *= 2;
     // wide groups settle for one round of wave slots before cutting finer
     const long long min_waves = waves > 1 ? kAutoMinItems / 2 : kAutoMinItems;

@@ -6,21 +6,25 @@
 // launching and retiring them while CUs wait for real work (measured: on a
 // log-uniform length mix the number of live waves sagged from 2048 to ~1200
 // in the middle of the launch).  Instead, every work-group decodes its own
-// index into the list of *live* items, ordered partition-major
-//     row p = all (sequence, kv head) pairs whose context reaches partition p,
-//             kv head fastest,
-// so all live items are dispatched first and the surplus work-groups (the
-// grid is sized for the worst case) are at the end and exit at once.  Within
-// a row, consecutive items are different kv heads of the same sequence and
-// (with the dispatcher dealing work-groups round-robin to the 8 XCDs) the
-// same (kv head, partition) of different sequences shares an XCD, so a
-// prompt prefix shared by the batch is read from that XCD's L2.
+// index into the list of *live* items, so all live items are dispatched first
+// and the surplus work-groups (the grid is sized for the worst case) are at
+// the end and exit at once.  The list is ordered longest first, so the last
+// items to start are the shortest and the launch ends evenly:
+//   1. every full partition (exactly P tokens), partition-major:
+//        row p = all (sequence, kv head) pairs with more than p full
+//        partitions, kv head fastest;
+//   2. then each sequence's last, partly filled partition (and the single
+//      empty item of a zero-length sequence), by decreasing token count, ties
+//      by sequence index, kv head fastest.
+// Within a row of part 1, consecutive items are different kv heads of the
+// same sequence and (with the dispatcher dealing work-groups round-robin to
+// the 8 XCDs) the same (kv head, partition) of different sequences shares an
+// XCD, so a prompt prefix shared by the batch is read from that XCD's L2.
 //
 // The decode is done by one wave from the context lengths alone: every lane
-// keeps the partition counts of up to kSchedMaxSeqs / 64 sequences in
-// registers, the row is found by a binary search over partition indices and
-// the sequence within the row with ballots.  A sequence of length 0 counts as
-// one item (its output row must be written as zeros).
+// keeps the counts of up to kSchedMaxSeqs / 64 sequences in registers; a row
+// of part 1 is found by a binary search over partition indices, a rank of
+// part 2 by a binary search over token counts, and the sequence with ballots.
 #pragma once
 
 #include "pa_device.h"
@@ -46,60 +50,96 @@ __device__ __forceinline__ int wave_sum_int(int x) {
            __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
 }
 
-// Item `item` of the partition-major live list.  Rows shrink with p, so the
-// number of items before row p, Hkv * sum_s min(np_s, p), is monotonic in p
-// and the row is found by binary search; the sequence is then the
-// rank-th one (in order) whose context reaches partition p.
-__device__ __forceinline__ WorkItem decode_work_item(const int32_t *seq_lens, int S, int Hkv,
-                                                     int part_tokens, int max_parts,
-                                                     long long item) {
-    const int lane = threadIdx.x & 63;
-    int np[kSchedChunks];
-#pragma unroll
-    for (int c = 0; c < kSchedChunks; ++c) {
-        const int s = 64 * c + lane;
-        int n = 0;
-        if (s < S) {
-            const int L = seq_lens[s];
-            n = L > 0 ? (L + part_tokens - 1) / part_tokens : 1;
-        }
-        np[c] = n;
-    }
-    const int nchunks = (S + 63) >> 6;
-    auto items_before_row = [&](int p) -> long long {
-        int acc = 0;
-#pragma unroll
-        for (int c = 0; c < kSchedChunks; ++c)
-            if (c < nchunks) acc += min(np[c], p);
-        return (long long)Hkv * wave_sum_int(acc);
-    };
-    if (item >= items_before_row(max_parts)) return WorkItem{0, 0, 0, false};
-    int lo = 0, hi = max_parts - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (items_before_row(mid) <= item) lo = mid;
-        else hi = mid - 1;
-    }
-    const int p = lo;
-    const long long idx = item - items_before_row(p);
-    int rank = (int)(idx / Hkv);
-    const int kvh = (int)(idx % Hkv);
+// The sequence holding the rank-th set predicate (in lane / chunk order).
+__device__ __forceinline__ int select_rank(const bool (&pred)[kSchedChunks], int nchunks, int rank) {
 #pragma unroll
     for (int c = 0; c < kSchedChunks; ++c) {
         if (c < nchunks) {
-            const unsigned long long m = __ballot(np[c] > p);
+            const unsigned long long m = __ballot(pred[c]);
             const int k = __popcll(m);
             if (rank < k) {
                 // the lane whose predicate is set with `rank` set lanes below it
                 const unsigned below = __builtin_amdgcn_mbcnt_hi(
                     (unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-                const unsigned long long hm = __ballot((np[c] > p) && (int)below == rank);
-                return WorkItem{64 * c + __ffsll((long long)hm) - 1, kvh, p, true};
+                const unsigned long long hm = __ballot(pred[c] && (int)below == rank);
+                return 64 * c + __ffsll((long long)hm) - 1;
             }
             rank -= k;
         }
     }
-    return WorkItem{0, 0, 0, false};
+    return -1;
+}
+
+// Item `item` of the live list (order above).
+__device__ __forceinline__ WorkItem decode_work_item(const int32_t *seq_lens, int S, int Hkv,
+                                                     int part_tokens, int max_parts,
+                                                     long long item) {
+    const int lane = threadIdx.x & 63;
+    int nf[kSchedChunks];    // full partitions
+    int key[kSchedChunks];   // tokens of the last partial partition; 0: empty sequence; -1: none
+#pragma unroll
+    for (int c = 0; c < kSchedChunks; ++c) {
+        const int s = 64 * c + lane;
+        int f = 0, k = -1;
+        if (s < S) {
+            const int L = seq_lens[s];
+            f = L / part_tokens;
+            const int r = L - f * part_tokens;
+            k = (r > 0 || L == 0) ? r : -1;
+        }
+        nf[c] = f;
+        key[c] = k;
+    }
+    const int nchunks = (S + 63) >> 6;
+    auto full_before_row = [&](int p) -> long long {
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < kSchedChunks; ++c)
+            if (c < nchunks) acc += min(nf[c], p);
+        return (long long)Hkv * wave_sum_int(acc);
+    };
+    auto count_key_at_least = [&](int v) -> int {
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < kSchedChunks; ++c)
+            if (c < nchunks) acc += key[c] >= v ? 1 : 0;
+        return wave_sum_int(acc);
+    };
+    const long long n_full = full_before_row(max_parts);
+    if (item < n_full) {
+        int lo = 0, hi = max_parts - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (full_before_row(mid) <= item) lo = mid;
+            else hi = mid - 1;
+        }
+        const int p = lo;
+        const long long idx = item - full_before_row(p);
+        bool pred[kSchedChunks];
+#pragma unroll
+        for (int c = 0; c < kSchedChunks; ++c) pred[c] = nf[c] > p;
+        const int s = select_rank(pred, nchunks, (int)(idx / Hkv));
+        return WorkItem{s, (int)(idx % Hkv), p, s >= 0};
+    }
+    const long long idx = item - n_full;
+    const int rank = (int)(idx / Hkv);
+    if (idx >= (long long)Hkv * count_key_at_least(0)) return WorkItem{0, 0, 0, false};
+    // largest v with more than `rank` keys >= v: the key of the rank-th item
+    int lo = 0, hi = part_tokens - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (count_key_at_least(mid) > rank) lo = mid;
+        else hi = mid - 1;
+    }
+    const int v = lo;
+    const int before = lo + 1 < part_tokens ? count_key_at_least(lo + 1) : 0;
+    bool pred[kSchedChunks];
+#pragma unroll
+    for (int c = 0; c < kSchedChunks; ++c) pred[c] = key[c] == v;
+    const int s = select_rank(pred, nchunks, rank - before);
+    if (s < 0) return WorkItem{0, 0, 0, false};
+    const int L = seq_lens[s];
+    return WorkItem{s, (int)(idx % Hkv), L / part_tokens, true};
 }
 
 }  // namespace pa
