@@ -36,7 +36,7 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
     constexpr int W = (G + 15) / 16;          // waves per work-group = 32-token sub-tiles per iteration
     int s, kvh, p;
     if (a.compact) {
-        // 1-D grid over the live items, partition-major (see pa_sched.h)
+        // 1-D grid over the live items, longest first (see pa_sched.h)
         const WorkItem w = decode_work_item(a.seq_lens, a.S, a.Hkv, a.part_tokens, a.max_parts,
                                             blockIdx.x);
         if (!w.valid) return;

@@ -103,7 +103,7 @@ template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
 __global__ __launch_bounds__(64) void valu_kernel(Args a) {
     int s, kvh, p;
     if (a.compact) {
-        // 1-D grid over the live items, partition-major (see pa_sched.h)
+        // 1-D grid over the live items, longest first (see pa_sched.h)
         const WorkItem w = decode_work_item(a.seq_lens, a.S, a.Hkv, a.part_tokens, a.max_parts,
                                             blockIdx.x);
         if (!w.valid) return;
