@@ -81,14 +81,24 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C / C++ source without comments and with whitespace collapsed (a record
+    stays valid across comment edits; the sources hold no comment markers
+    inside string literals)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha256(kernel: str) -> str:
-    """Hash of one kernel's source files (ties hardware-counter records to a build)."""
+    """Hash of one kernel's source code (ties hardware-counter records to a build)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_301_amd", "csrc")
     for name in sorted(KERNEL_SOURCES[kernel]):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 
