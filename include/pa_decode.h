@@ -228,6 +228,24 @@ pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_
 pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int n,
                          int Hkv, int D, int B, int NB, pa_dtype dtype, void *stream);
 
+/*
+ * pa_check_inputs -- debug check of the device-data preconditions above
+ * (0 <= seq_lens[s] <= max_blocks * B; 0 <= block_tables[s][j] < NB for every
+ * j < ceil(seq_lens[s] / B)), run on the device without reading K or V.
+ *
+ *   report   int32[2], device, caller-owned: report[0] = number of offending
+ *            sequences, report[1] = smallest offending sequence index
+ *            (INT32_MAX if none).  Written by the call (no prior zeroing).
+ *
+ * Only the table entries a valid length would use are read, so any table is
+ * safe to check.  Run it before pa_decode / pa_prefill / pa_append_kv on
+ * untrusted inputs and skip the call when report[0] != 0.  Asynchronous on
+ * `stream`.  Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_HIP.  S = 0 writes a
+ * clean report.
+ */
+pa_status pa_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int S,
+                          int max_blocks, int B, int NB, int32_t *report, void *stream);
+
 const char *pa_status_string(pa_status status);
 
 #ifdef __cplusplus

@@ -90,6 +90,8 @@ def load():
     lib.pa_prefill.restype = _INT
     lib.pa_prefill.argtypes = ([_PTR] * 6 + [ctypes.c_float, _PTR] + mq_shape +
                                [ctypes.POINTER(PaConfig), _PTR, ctypes.c_size_t, _PTR])
+    lib.pa_check_inputs.restype = _INT
+    lib.pa_check_inputs.argtypes = [_PTR, _PTR] + [_INT] * 4 + [_PTR, _PTR]
     lib.pa_copy_blocks.restype = _INT
     lib.pa_copy_blocks.argtypes = [_PTR] * 3 + [_INT] * 6 + [_PTR]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -166,12 +168,16 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
            out: Optional[torch.Tensor] = None, *, out_dtype: Optional[torch.dtype] = None,
            kernel="auto", partition_tokens: int = 0, stages: int = 0, kv_reuse: bool = False,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, stream=None,
+           check: Optional[bool] = None) -> torch.Tensor:
     """Paged decode attention: out[S,Hq,D] from query[S,Hq,D], K/V pools
     [NB,Hkv,B,D], block_tables[S,max_blocks] int32 and seq_lens[S] int32.
 
     All tensors must be contiguous and on the same GPU.  Asynchronous on
-    ``stream`` (default: torch's current stream).
+    ``stream`` (default: torch's current stream).  ``check`` (default: the
+    PA_CHECK=1 environment variable) first verifies the lengths and table
+    entries on the device and raises InputCheckError instead of launching
+    (this synchronises the stream).
     """
     lib = load()
     for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
@@ -195,6 +201,8 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     shape = _shape_args(query, key_cache, block_tables, out_dtype)
     if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
         raise ValueError("seq_lens / block_tables do not match the batch size")
+    if _checking(check):
+        _run_check(block_tables, seq_lens, key_cache, stream)
     cfg = _config(kernel, partition_tokens, stages, kv_reuse)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
@@ -227,12 +235,13 @@ def plan_prefill(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype, out_
 def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start, scale,
             out=None, *, max_query_len: Optional[int] = None, out_dtype=None, kernel="auto",
             partition_tokens: int = 0, stages: int = 0, kv_reuse: bool = False,
-            workspace=None, stream=None) -> torch.Tensor:
+            workspace=None, stream=None, check: Optional[bool] = None) -> torch.Tensor:
     """Causal attention of several new tokens per sequence: out[T,Hq,D] from
     query[T,Hq,D] (rows grouped by sequence, query_start[S+1] int32), the
     paged K/V pools and block_tables / seq_lens (lengths count the new
     tokens).  ``max_query_len`` (the largest n_s) is read back from
-    query_start when not given, which synchronises the stream."""
+    query_start when not given, which synchronises the stream.  ``check`` as
+    in ``decode``."""
     lib = load()
     for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
                     ("block_tables", block_tables), ("seq_lens", seq_lens),
@@ -265,6 +274,8 @@ def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start, 
         raise ValueError("out must be a contiguous [T,Hq,D] tensor of out_dtype")
     shape = (S, T, Hq, Hkv, D, B, NB, block_tables.shape[1], int(max_query_len),
              _TORCH_TO_PA[query.dtype], _TORCH_TO_PA[out_dtype])
+    if _checking(check):
+        _run_check(block_tables, seq_lens, key_cache, stream)
     cfg = _config(kernel, partition_tokens, stages, kv_reuse)
     p = PaPlan()
     _check(lib.pa_prefill_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
@@ -285,6 +296,46 @@ def prefill_workload(pw, **kw) -> torch.Tensor:
     w = pw.base
     return prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
                    pw.query_start, w.scale, max_query_len=pw.max_query_len, **kw)
+
+
+class InputCheckError(ValueError):
+    """Lengths or block-table entries violate the documented preconditions."""
+
+
+def check_inputs(block_tables, seq_lens, num_blocks: int, block_size: int, stream=None):
+    """Run the device check of lengths and used table entries; returns
+    (number of offending sequences, smallest offending index or None).
+    Synchronises the stream."""
+    lib = load()
+    if not (block_tables.is_cuda and seq_lens.is_cuda):
+        raise ValueError("tensors must be on the GPU")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if not (block_tables.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("tensors must be contiguous")
+    S = seq_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, max_blocks]")
+    report = torch.empty(2, dtype=torch.int32, device=seq_lens.device)
+    st = _stream_handle(stream, seq_lens.device)
+    _check(lib.pa_check_inputs(block_tables.data_ptr(), seq_lens.data_ptr(), S,
+                               block_tables.shape[1], block_size, num_blocks,
+                               report.data_ptr(), st))
+    bad, first = report.cpu().tolist()
+    return bad, (first if bad else None)
+
+
+def _checking(check) -> bool:
+    return bool(check) if check is not None else os.environ.get("PA_CHECK", "0") == "1"
+
+
+def _run_check(block_tables, seq_lens, key_cache, stream):
+    NB, _, B, _ = key_cache.shape
+    bad, first = check_inputs(block_tables, seq_lens, NB, B, stream)
+    if bad:
+        raise InputCheckError(
+            f"{bad} sequence(s) violate the length / block-table preconditions "
+            f"(first: sequence {first}); nothing was launched")
 
 
 def _stream_handle(stream, device):
@@ -455,11 +506,14 @@ class PreparedCall:
 
 def prepare(query, key_cache, value_cache, block_tables, seq_lens, scale, out, *,
             kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, workspace=None,
-            stream=None) -> PreparedCall:
-    """Validate once (by running the same checks as ``decode`` on a plan) and
+            stream=None, check: Optional[bool] = None) -> PreparedCall:
+    """Validate once (by running the same checks as ``decode`` on a plan, and
+    with ``check`` the device check of the current lengths and tables) and
     return a PreparedCall that launches the configured stage(s)."""
     lib = load()
     shape = _shape_args(query, key_cache, block_tables, out.dtype)
+    if _checking(check):
+        _run_check(block_tables, seq_lens, key_cache, stream)
     cfg = _config(kernel, partition_tokens, stages, kv_reuse)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))

@@ -468,6 +468,16 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pair
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int S,
+                          int max_blocks, int B, int NB, int32_t *report, void *stream) {
+    if (S < 0 || max_blocks < 0 || B <= 0 || NB <= 0) return PA_ERR_SHAPE;
+    if (!report) return PA_ERR_NULL;
+    if (S > 0 && (!seq_lens || (max_blocks > 0 && !block_tables))) return PA_ERR_NULL;
+    const hipError_t err = pa::launch_check(block_tables, seq_lens, S, max_blocks, B, NB, report,
+                                            static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 const char *pa_status_string(pa_status status) {
     switch (status) {
     case PA_OK: return "PA_OK";

@@ -42,6 +42,8 @@ hipError_t launch_valu(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st)
 hipError_t launch_mfma(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
 hipError_t launch_combine(const Args &a, pa_dtype odt, hipStream_t st);
 hipError_t launch_prefill(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t st);
+hipError_t launch_check(const int32_t *block_tables, const int32_t *seq_lens, int S,
+                        int max_blocks, int B, int NB, int32_t *report, hipStream_t st);
 
 // (query token, head) columns per work-group of the multi-token matrix-core
 // kernel: four waves of four 16-column groups.

@@ -125,3 +125,13 @@ def test_kv_write_validation(lib):
     assert lib.pa_append_kv(fake, fake, fake, fake, fake, fake, 2, 2, 8, 4, 4, -1, F16, None) == b.PA_ERR_SHAPE
     assert lib.pa_append_kv(fake, fake, None, fake, fake, fake, 2, 2, 8, 4, 4, 3, F16, None) == b.PA_ERR_NULL
     assert lib.pa_append_kv(None, None, None, None, None, None, 0, 2, 8, 4, 4, 3, F16, None) == b.PA_OK
+
+
+def test_check_inputs_validation(lib):
+    fake = 1 << 20
+    assert lib.pa_check_inputs(fake, fake, -1, 4, 16, 8, fake, None) == b.PA_ERR_SHAPE
+    assert lib.pa_check_inputs(fake, fake, 2, 4, 0, 8, fake, None) == b.PA_ERR_SHAPE
+    assert lib.pa_check_inputs(fake, fake, 2, 4, 16, 0, fake, None) == b.PA_ERR_SHAPE
+    assert lib.pa_check_inputs(fake, fake, 2, 4, 16, 8, None, None) == b.PA_ERR_NULL
+    assert lib.pa_check_inputs(fake, None, 2, 4, 16, 8, fake, None) == b.PA_ERR_NULL
+    assert lib.pa_check_inputs(None, fake, 2, 4, 16, 8, fake, None) == b.PA_ERR_NULL

@@ -292,3 +292,34 @@ def test_many_sequences(kernel, Hq, Hkv, S):
     w = workloads.make_workload(spec, device=DEV, poison=True)
     out = run(w, out_dtype=torch.float32, kernel=kernel, partition_tokens=64)
     check(out, oracle_full(w), torch.bfloat16, f"{kernel}/S{S}")
+
+
+# ------------------------------------------------------- precondition check
+
+def test_check_inputs_reports_bad_tables_and_lengths():
+    """The device check counts exactly the sequences whose length or used
+    table entries break the preconditions; the binding refuses to launch on
+    them.  (No attention kernel ever sees the bad inputs.)"""
+    say("case: device check of lengths and block tables")
+    spec = workloads.WorkloadSpec("chk", S=6, Hq=8, Hkv=2, D=128, B=16, dtype="bf16",
+                                  lens=("fixed", (0, 1, 16, 17, 100, 160)), max_len=160,
+                                  pool=("free", 0.2), seed=41)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    assert binding.check_inputs(w.block_tables, w.seq_lens, w.NB, w.B) == (0, None)
+    bt = w.block_tables.clone()
+    sl = w.seq_lens.clone()
+    bt[3, 1] = w.NB                # used entry (17 tokens: blocks 0, 1) out of range
+    bt[4, 0] = -1                  # negative id
+    bt[5, 9] = w.NB + 7            # last used entry of a full 160-token context
+    bt[2, 5] = -5                  # past ceil(16 / 16) = 1: never read, not an error
+    sl[1] = w.max_blocks * w.B + 1 # longer than the table
+    assert binding.check_inputs(bt, sl, w.NB, w.B) == (4, 1)
+    sl2 = w.seq_lens.clone()
+    sl2[0] = -3
+    assert binding.check_inputs(w.block_tables, sl2, w.NB, w.B) == (1, 0)
+    with pytest.raises(binding.InputCheckError):
+        binding.decode(w.query, w.key_cache, w.value_cache, bt, sl, w.scale, check=True)
+    out = binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                         w.scale, out_dtype=torch.float32, check=True)
+    torch.cuda.synchronize()
+    check(out, oracle_full(w), torch.bfloat16, "checked decode")
