@@ -313,6 +313,46 @@ def test_exhaustive_tiny_tables():
         assert np.max(np.abs(outs[0] - ref)) < 1e-14
 
 
+def _brute_force_row(q, Kl, Vl, scale):
+    """Attention of one query over logical rows, in plain Python with fsum."""
+    x = [scale * math.fsum(a * b for a, b in zip(q, k)) for k in Kl]
+    m = max(x)
+    w = [math.exp(v - m) for v in x]
+    z = math.fsum(w)
+    return [math.fsum(wi * v[d] for wi, v in zip(w, Vl)) / z for d in range(len(q))]
+
+
+def test_brute_force_small_cases():
+    """B in 1..4, L in 1..9, D in 1..3, group 1 or 2, tables drawn from a
+    shuffled pool (at least 6 blocks): the oracle equals nested-loop Python."""
+    rnd = np.random.default_rng(77)
+    for B in (1, 2, 3, 4):
+        for L in range(1, 10):
+            for D in (1, 2, 3):
+                for G in (1, 2):
+                    nb = -(-L // B)
+                    NB = max(6, nb)
+                    Kl = rnd.standard_normal((L, D))
+                    Vl = rnd.standard_normal((L, D))
+                    q = rnd.standard_normal((G, D))
+                    table = rnd.permutation(NB)[:nb]
+                    kc = torch.full((NB, 1, B, D), float("nan"), dtype=torch.float32)
+                    vc = kc.clone()
+                    for t in range(L):
+                        kc[table[t // B], 0, t % B] = torch.from_numpy(Kl[t]).float()
+                        vc[table[t // B], 0, t % B] = torch.from_numpy(Vl[t]).float()
+                    Kf = kc.double()
+                    Vf = vc.double()
+                    K32 = [[float(Kf[table[t // B], 0, t % B, d]) for d in range(D)] for t in range(L)]
+                    V32 = [[float(Vf[table[t // B], 0, t % B, d]) for d in range(D)] for t in range(L)]
+                    qt = torch.from_numpy(q).float().reshape(1, G, D)
+                    out = oracle.decode(qt, kc, vc, torch.from_numpy(table[None].astype(np.int32)),
+                                        torch.tensor([L], dtype=torch.int32), 0.6)
+                    for h in range(G):
+                        ref = _brute_force_row([float(v) for v in qt[0, h].double()], K32, V32, 0.6)
+                        assert np.max(np.abs(out[0, h] - np.array(ref))) < 1e-14, (B, L, D, G)
+
+
 def test_rejects_out_of_range_inputs():
     q = torch.zeros((1, 1, 2))
     kc = torch.zeros((2, 1, 2, 2))
