@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--kv-reuse", choices=["on", "off"], default="off",
                     help="cached (on) or streamed (off, default) K/V loads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="decode: extra calls timed after writing a 1 GiB scratch buffer "
+                         "(evicts the L2s and the last-level cache); 0 to skip")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--print-source-sha", action="store_true",
@@ -67,7 +70,7 @@ def parse():
 
 # Sources each kernel is built from: a traffic record stays valid while these
 # files are unchanged.
-_COMMON = ["pa_device.h", "pa_internal.h"]
+_COMMON = ["pa_device.h", "pa_args.h"]
 KERNEL_SOURCES = {
     "pa_valu_partitions": ["pa_valu.hip", "pa_tile.h", "pa_table.h", "pa_sched.h"] + _COMMON,
     "pa_mfma_partitions": ["pa_mfma.hip", "pa_mfma_core.h", "pa_tile.h", "pa_table.h",
@@ -482,6 +485,27 @@ def main():
           f"(min {part_ms.min() * 1e3:.1f}), combine avg {comb_ms.mean() * 1e3:.1f} us, "
           f"step {step_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # cold cache: the same step after a 1 GiB scratch write (outside the events)
+    cold = None
+    if args.cold_calls > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for i in range(args.cold_calls):
+            scratch.fill_(i & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            step(e)
+            torch.cuda.synchronize()
+            cold_ms.append(e[0].elapsed_time(e[2]))
+        del scratch
+        c = np.array(cold_ms)
+        cold = {"calls": args.cold_calls, "median_us": round(float(np.median(c)) * 1e3, 2),
+                "p10_us": round(float(np.percentile(c, 10)) * 1e3, 2),
+                "p90_us": round(float(np.percentile(c, 90)) * 1e3, 2),
+                "gbs_median": round(kv / (float(np.median(c)) * 1e-3) / 1e9, 2)}
+    esz = w.esz
+    n_blocks = int(((w.lens + w.B - 1) // w.B).sum())
+    alg_total = kv + 2 * w.S * w.Hq * w.D * esz + 4 * n_blocks + 4 * w.S
+
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -504,7 +528,13 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),
         "kernel_us": {"partitions": round(part_avg * 1e3, 2),
+                      "partitions_p10": round(float(np.percentile(part_ms, 10)) * 1e3, 2),
+                      "partitions_p90": round(float(np.percentile(part_ms, 90)) * 1e3, 2),
                       "combine": round(float(comb_ms.mean()) * 1e3, 2)},
+        "cold_cache": cold,
+        "alg_bytes_total": alg_total,
+        "workspace_bytes": plan["workspace_bytes"],
+        "flops_alg": int(w.lens.sum()) * w.Hq * 4 * w.D,
         "roofline": {"bound": "hbm", "kernel": f"pa_{kname}_partitions",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

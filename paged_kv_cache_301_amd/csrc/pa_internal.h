@@ -1,5 +1,5 @@
-// pa_internal.h -- argument block and launcher declarations shared by the
-// host entry points (pa_api.cpp) and the kernel files.  Not part of the ABI.
+// pa_internal.h -- launcher declarations shared by the host entry points
+// (pa_api.cpp) and the kernel files.  Not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,33 +7,9 @@
 #include <cstdint>
 
 #include "pa_decode.h"
+#include "pa_args.h"
 
 namespace pa {
-
-// Everything one launch needs, passed to kernels by value (kernarg segment).
-struct Args {
-    const void *query;        // [S][Hq][D]
-    const void *key_cache;    // [NB][Hkv][B][D]
-    const void *value_cache;  // [NB][Hkv][B][D]
-    const int32_t *block_tables;  // [S][max_blocks]
-    const int32_t *seq_lens;      // [S]
-    void *out;                // [S][Hq][D] (out dtype)
-    float *part_o;            // [S][Hq][max_parts][D]   split plans only
-    float *part_m;            // [S][Hq][max_parts]      running max, log2 units
-    float *part_l;            // [S][Hq][max_parts]      sum of weights
-    float scale_log2;         // scale * log2(e): scores live in exp2 units
-    int S, Hq, Hkv, D, B, NB, max_blocks;
-    int log2B;                // log2(B) when B is a power of two, else -1
-    int part_tokens;          // tokens per context partition
-    int max_parts;            // partitions per (s, head) in the grid
-    int split;                // 1: write partials, 0: write final output
-    int stream_kv;            // 1: K / V loads carry the non-temporal hint
-    int compact;              // 1: 1-D grid decoded into live items (pa_sched.h)
-    // Multi-token (causal) calls only; query_start is null for decode.
-    const int32_t *query_start;   // [S+1] rows query_start[s] .. query_start[s+1]-1 are sequence s's
-    int T;                        // query rows; query / out are [T][Hq][D]
-    int q_blocks;                 // query blocks per sequence in the grid
-};
 
 // Launchers return hipErrorInvalidValue when no instantiation covers the
 // requested shape / types (the host checks support before calling).
@@ -45,21 +21,11 @@ hipError_t launch_prefill(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t 
 hipError_t launch_check(const int32_t *block_tables, const int32_t *seq_lens, int S,
                         int max_blocks, int B, int NB, int32_t *report, hipStream_t st);
 
-// (query token, head) columns per work-group of the multi-token matrix-core
-// kernel: four waves of four 16-column groups.
-constexpr int kPrefillColumns = 128;
 hipError_t launch_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
                            const int32_t *block_tables, const int32_t *seq_lens,
                            void *key_cache, void *value_cache, int T, int Hkv, int D, int B,
                            int NB, int max_blocks, int esz, hipStream_t st);
 hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int n,
                               long long block_bytes, int NB, hipStream_t st);
-
-// Tokens one loop iteration of the tiled kernels covers; partitions are
-// multiples of this.
-constexpr int kTileTokens = 32;
-
-// Partitions per (sequence, head): the partition index is grid dimension y.
-constexpr int kMaxPartitions = 65535;
 
 }  // namespace pa
