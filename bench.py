@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--kv-reuse", choices=["on", "off"], default="off",
                     help="cached (on) or streamed (off, default) K/V loads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-peak", action="store_true",
+                    help="decode: skip the plain 4 GiB device read used as the measured HBM peak")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="decode: extra calls timed after writing a 1 GiB scratch buffer "
                          "(evicts the L2s and the last-level cache); 0 to skip")
@@ -120,6 +122,32 @@ def recorded_traffic(kernel: str, workload: str, block_size: int):
             if (m.group(1), m.group(2), int(m.group(3)), m.group(4)) == (kernel, workload, block_size, sha):
                 return int(m.group(5)) + int(m.group(6))
     return None
+
+
+def measured_read_peak(dev, calls=5):
+    """Achievable HBM read rate: the library's plain streaming read (16-byte
+    non-temporal loads, as the paged kernels use) over a 4 GiB buffer, far
+    larger than every cache level; median of a few calls after one warm-up."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_301_amd import binding
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    binding.read_bytes(buf, sink, stream=stream)
+    ms = []
+    for _ in range(calls):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        binding.read_bytes(buf, sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del buf
+    med = float(np.median(ms))
+    return {"gbs": round(nbytes / (med * 1e-3) / 1e9, 2), "bytes": nbytes,
+            "kernel": "pa_read_bytes over a 4 GiB buffer", "calls": calls}
 
 
 def cpu_baseline(w, target_s):
@@ -540,6 +568,10 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"pa_{kname}_partitions", args.workload, w.B)},
     }
+    if not args.no_read_peak:
+        peak = measured_read_peak(dev)
+        peak["step_frac"] = round(gbs / peak["gbs"], 4)
+        res["read_peak_measured"] = peak
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -74,9 +74,10 @@ typedef enum {
                                two, groups of 1, 2, 4 or 8 query heads; 16-byte
                                loads of whole block rows, VALU dot products     */
     PA_KERNEL_MFMA = 3      /* grouped-query kernel: D = 128, fp16 / bf16, B a
-                               power of two, 4, 8, 16, 32 or 64 query heads per
-                               kv head (32 and 64: multi-query, several waves
-                               share each K / V tile); the group's q.K and p.V
+                               power of two, 1, 2, 4, 8, 16, 32 or 64 query
+                               heads per kv head (32 and 64: multi-query,
+                               several waves share each K / V tile; 1 and 2
+                               only when asked for); the group's q.K and p.V
                                contractions on matrix cores                      */
 } pa_kernel;
 

@@ -94,6 +94,8 @@ def load():
     lib.pa_check_inputs.argtypes = [_PTR, _PTR] + [_INT] * 4 + [_PTR, _PTR]
     lib.pa_copy_blocks.restype = _INT
     lib.pa_copy_blocks.argtypes = [_PTR] * 3 + [_INT] * 6 + [_PTR]
+    lib.pa_read_bytes.restype = _INT
+    lib.pa_read_bytes.argtypes = [_PTR, ctypes.c_size_t, _PTR, _PTR]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [_INT]
     # host block pool
@@ -404,6 +406,19 @@ def copy_blocks(key_cache, value_cache, pairs, stream=None):
     _check(lib.pa_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(), pairs.data_ptr(),
                               pairs.shape[0], Hkv, D, B, NB, _TORCH_TO_PA[key_cache.dtype],
                               _stream_handle(stream, key_cache.device)))
+
+
+def read_bytes(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Stream the bytes of a contiguous GPU tensor through the library's plain
+    read kernel once (the achievable-read reference); sink: a GPU tensor of at
+    least 4 bytes that the kernel may write."""
+    lib = load()
+    if not (buf.is_cuda and sink.is_cuda):
+        raise ValueError("tensors must be on the GPU")
+    if not buf.is_contiguous() or sink.numel() * sink.element_size() < 4:
+        raise ValueError("buf must be contiguous and sink at least 4 bytes")
+    _check(lib.pa_read_bytes(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                             _stream_handle(stream, buf.device)))
 
 
 class BlockPool:

@@ -27,5 +27,6 @@ hipError_t launch_kv_write(const void *key, const void *value, const int32_t *sl
                            int NB, int max_blocks, int esz, hipStream_t st);
 hipError_t launch_copy_blocks(void *key_cache, void *value_cache, const int32_t *pairs, int n,
                               long long block_bytes, int NB, hipStream_t st);
+hipError_t launch_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
 
 }  // namespace pa

@@ -172,6 +172,8 @@ hipError_t launch_g(const Args &a, hipStream_t st) {
 template <typename T, typename OutT>
 hipError_t launch_t(const Args &a, hipStream_t st) {
     switch (a.Hq / a.Hkv) {
+    case 1: return launch_g<T, OutT, 1>(a, st);
+    case 2: return launch_g<T, OutT, 2>(a, st);
     case 4: return launch_g<T, OutT, 4>(a, st);
     case 8: return launch_g<T, OutT, 8>(a, st);
     case 16: return launch_g<T, OutT, 16>(a, st);

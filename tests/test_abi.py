@@ -58,7 +58,7 @@ def test_validation_errors(lib):
     assert _call(lib, cfg=cfg) == b.PA_ERR_WORKSPACE
     assert _call(lib, cfg=cfg, ws=1 << 20, ws_bytes=16) == b.PA_ERR_WORKSPACE
     # forced kernel that cannot run the shape
-    assert _call(lib, cfg=b.PaConfig(b.KERNEL_MFMA, 0, 0), Hq=4, Hkv=4) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_MFMA, 0, 0), Hq=12, Hkv=4) == b.PA_ERR_UNSUPPORTED
     assert _call(lib, cfg=b.PaConfig(b.KERNEL_VALU, 0, 0), D=64) == b.PA_ERR_UNSUPPORTED
     assert _call(lib, cfg=b.PaConfig(9, 0, 0)) == b.PA_ERR_UNSUPPORTED
     # partition not a multiple of 32
@@ -70,10 +70,14 @@ def test_empty_batch_is_noop(lib):
 
 
 def test_plans():
+    # one head per kv head: the VALU kernel unless the matrix cores are asked for
     p = b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16)
-    assert p["kernel"] == b.KERNEL_VALU and p["split"] == 1
+    assert p["kernel"] == b.KERNEL_VALU and p["split"] == 1 and p["partition_tokens"] == 1024
     assert p["max_partitions"] * p["partition_tokens"] >= 256 * 16
     assert p["workspace_bytes"] >= 64 * 32 * p["max_partitions"] * (128 + 2) * 4
+    assert b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16,
+                  kernel="mfma")["kernel"] == b.KERNEL_MFMA
+    assert b.plan(8, 16, 8, 128, 16, 645, 128, torch.float16)["kernel"] == b.KERNEL_VALU
     p = b.plan(128, 64, 8, 128, 16, 100, 512, torch.bfloat16)
     assert p["kernel"] == b.KERNEL_MFMA
     p = b.plan(1, 1, 1, 2, 2, 8, 3, torch.float32)
@@ -125,6 +129,15 @@ def test_kv_write_validation(lib):
     assert lib.pa_append_kv(fake, fake, fake, fake, fake, fake, 2, 2, 8, 4, 4, -1, F16, None) == b.PA_ERR_SHAPE
     assert lib.pa_append_kv(fake, fake, None, fake, fake, fake, 2, 2, 8, 4, 4, 3, F16, None) == b.PA_ERR_NULL
     assert lib.pa_append_kv(None, None, None, None, None, None, 0, 2, 8, 4, 4, 3, F16, None) == b.PA_OK
+
+
+def test_read_bytes_validation(lib):
+    fake = 1 << 20
+    assert lib.pa_read_bytes(None, 0, None, None) == b.PA_OK
+    assert lib.pa_read_bytes(None, 64, fake, None) == b.PA_ERR_NULL
+    assert lib.pa_read_bytes(fake, 64, None, None) == b.PA_ERR_NULL
+    assert lib.pa_read_bytes(fake, 24, fake, None) == b.PA_ERR_SHAPE
+    assert lib.pa_read_bytes(fake + 4, 64, fake, None) == b.PA_ERR_SHAPE
 
 
 def test_check_inputs_validation(lib):

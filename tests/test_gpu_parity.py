@@ -95,6 +95,12 @@ SMALL = [
     ("mfma", "bf16", 16, 4, 2, 32),
     ("mfma", "bf16", 32, 2, 32, 64),
     ("mfma", "bf16", 16, 1, 64, 0),
+    # one or two heads per kv head, padded to 16 columns
+    ("mfma", "bf16", 8, 8, 16, 0),
+    ("mfma", "f16", 8, 8, 16, 64),
+    ("mfma", "bf16", 8, 8, 1, 96),
+    ("mfma", "bf16", 8, 4, 8, 0),
+    ("mfma", "f16", 4, 2, 32, 32),
     # groups wider than 16: several waves per work-group (MQA when Hkv = 1)
     ("mfma", "bf16", 32, 1, 16, 0),
     ("mfma", "f16", 64, 1, 16, 64),
@@ -137,7 +143,8 @@ def test_zero_length_rows_are_zero(kernel):
 
 NEEDLE_KERNELS = [("generic", 8, 2, 16, 0), ("valu", 8, 8, 16, 64), ("valu", 8, 8, 1, 64),
                   ("valu", 8, 4, 8, 0), ("mfma", 16, 2, 16, 64), ("mfma", 16, 4, 1, 96),
-                  ("mfma", 32, 4, 8, 0), ("mfma", 64, 1, 16, 64), ("mfma", 64, 2, 1, 0)]
+                  ("mfma", 32, 4, 8, 0), ("mfma", 64, 1, 16, 64), ("mfma", 64, 2, 1, 0),
+                  ("mfma", 8, 8, 16, 64), ("mfma", 8, 4, 1, 0)]
 
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,B,part", NEEDLE_KERNELS)
@@ -185,7 +192,7 @@ def test_needle_bit_exact(kernel, Hq, Hkv, B, part):
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,B,part", [("valu", 8, 8, 16, 64), ("mfma", 16, 2, 16, 64),
                                                   ("mfma", 16, 4, 1, 64), ("generic", 4, 2, 16, 0),
-                                                  ("mfma", 64, 1, 16, 64)])
+                                                  ("mfma", 64, 1, 16, 64), ("mfma", 8, 8, 16, 64)])
 def test_relabel_poison_determinism(kernel, Hq, Hkv, B, part):
     say(f"case: relabel/poison/determinism {kernel} B={B}")
     spec = workloads.WorkloadSpec("perm", S=4, Hq=Hq, Hkv=Hkv, D=128, B=B, dtype="bf16",
@@ -238,7 +245,8 @@ def test_stages_equal_one_call(kernel):
 
 FULL = [("mha_small", {}), ("mha_7b", {}), ("gqa_70b", {}), ("gqa_long", {"B": 16}),
         ("gqa_long", {"B": 1}), ("gqa_long", {"B": 8}), ("gqa_long", {"B": 32}),
-        ("mqa", {}), ("mqa", {"Hq": 32})]
+        ("mqa", {}), ("mqa", {"Hq": 32}), ("mha_7b", {"kernel": "mfma"}),
+        ("mha_small", {"kernel": "mfma"})]
 
 
 @pytest.mark.parametrize("name,over", FULL)
@@ -246,8 +254,10 @@ def test_full_size_sampled(name, over):
     """Full-size workload, automatic plan (what the benchmark times); 48
     sampled (sequence, head) rows against the oracle, plus finiteness of all."""
     say(f"case: full-size {name} {over}")
+    over = dict(over)
+    kernel = over.pop("kernel", "auto")
     w = workloads.make_workload(name, device=DEV, poison=True, **over)
-    out = run(w, out_dtype=torch.float32)
+    out = run(w, out_dtype=torch.float32, kernel=kernel)
     assert torch.isfinite(out).all()
     rng = np.random.default_rng(21)
     rows = rng.choice(w.S * w.Hq, size=min(48, w.S * w.Hq), replace=False)
@@ -259,7 +269,7 @@ def test_full_size_sampled(name, over):
     got = out.reshape(w.S * w.Hq, w.D)[torch.as_tensor(rows, device=DEV)]
     check(got, ref, w.dtype, name)
     # native-dtype output as well
-    out2 = run(w)
+    out2 = run(w, kernel=kernel)
     got2 = out2.reshape(w.S * w.Hq, w.D)[torch.as_tensor(rows, device=DEV)]
     check(got2, ref, w.dtype, name + "/native")
 
