@@ -107,20 +107,33 @@ def source_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(kernel: str, workload: str, block_size: int):
+def record_key(workload: str, args) -> str:
+    """Workload name of a traffic record: the named workload plus the
+    overrides that change its shape (query heads, new tokens per sequence)."""
+    key = workload
+    if args.q_heads:
+        key += f"_hq{args.q_heads}"
+    if args.op == "prefill" and args.new_tokens:
+        key += f"_new{args.new_tokens}"
+    return key
+
+
+def recorded_traffic(kernel: str, workload: str, block_size: int, partition: int = 0):
     """HBM bytes per launch from a rocprofv3 --pmc summary under profiles/,
-    if one was recorded for these exact kernel sources; else None."""
+    if one was recorded for these exact kernel sources and the same partition
+    size (0: the kernel has none); else None."""
     import glob
     import re
     if kernel not in KERNEL_SOURCES:
         return None
     sha = source_sha256(kernel)
-    pat = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) "
+    pat = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) P=(\d+) "
                      r"source_sha256=([0-9a-f]+) read_bytes=(\d+) write_bytes=(\d+)")
+    want = (kernel, workload, block_size, partition, sha)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for m in pat.finditer(open(path).read()):
-            if (m.group(1), m.group(2), int(m.group(3)), m.group(4)) == (kernel, workload, block_size, sha):
-                return int(m.group(5)) + int(m.group(6))
+            if (m.group(1), m.group(2), int(m.group(3)), int(m.group(4)), m.group(5)) == want:
+                return int(m.group(6)) + int(m.group(7))
     return None
 
 
@@ -270,7 +283,7 @@ def bench_write(args, w, dev):
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(kernel, f"{args.op}_{args.workload}", w.B)},
+                     "traffic": recorded_traffic(kernel, record_key(f"{args.op}_{args.workload}", args), w.B)},
     }
     if not args.no_cpu_baseline and args.op == "copy_blocks":
         from oracle.block_manager import copy_blocks as oracle_copy
@@ -388,7 +401,8 @@ def bench_prefill(args, dev):
         "kernel_us": {"partitions": round(k_ms * 1e3, 2), "combine": round(c_ms * 1e3, 2)},
         "roofline": {"bound": "mfma", "kernel": f"pa_prefill_{kname}", "achieved": round(achieved, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": recorded_traffic(f"pa_prefill_{kname}", f"prefill_{name}", w.B)},
+                     "traffic": recorded_traffic(f"pa_prefill_{kname}", record_key(f"prefill_{name}", args), w.B,
+                                                 plan["partition_tokens"])},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -566,7 +580,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": f"pa_{kname}_partitions",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"pa_{kname}_partitions", args.workload, w.B)},
+                     "traffic": recorded_traffic(f"pa_{kname}_partitions", record_key(args.workload, args), w.B,
+                                                 plan["partition_tokens"])},
     }
     if not args.no_read_peak:
         peak = measured_read_peak(dev)
