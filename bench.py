@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--kv-reuse", choices=["on", "off"], default="off",
                     help="cached (on) or streamed (off, default) K/V loads")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: also time the step captured in one HIP graph and replayed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-peak", action="store_true",
                     help="decode: skip the plain 4 GiB device read used as the measured HBM peak")
@@ -163,6 +165,18 @@ def measured_read_peak(dev, calls=5):
             "kernel": "pa_read_bytes over a 4 GiB buffer", "calls": calls}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the CPU baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, target_s):
     """Time the oracle on the host: whole batch, repeated until target_s."""
     import oracle
@@ -192,8 +206,8 @@ def cpu_baseline(w, target_s):
         oracle.decode(q, kc, vc, bt, sl, w.scale, rows=rows)
     dt = time.perf_counter() - t0
     return {"value": round(sample_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle", "sample": desc,
-            "seconds": round(dt, 2)}
+            "cores": oracle.num_threads(), "cpu": cpu_model(), "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 2)}
 
 
 def write_slots(w, T, seed=11):
@@ -298,7 +312,7 @@ def bench_write(args, w, dev):
             reps += 1
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(alg_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": 1, "cpu": cpu_model(), "kind": "oracle",
                                "sample": f"{T} block copies in a host pool of the {2 * T} blocks "
                                          f"they touch (the oracle also clones that pool), {reps} pass(es)",
                                "seconds": round(dt, 2)}
@@ -323,7 +337,7 @@ def bench_write(args, w, dev):
             reps += 1
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(alg_bytes * reps / dt / 1e9, 4), "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": 1, "cpu": cpu_model(), "kind": "oracle",
                                "sample": f"whole write ({T} tokens) into a host pool of the "
                                          f"{nb} blocks it touches, {reps} pass(es)",
                                "seconds": round(dt, 2)}
@@ -425,7 +439,8 @@ def bench_prefill(args, dev):
         L0, n_0 = int(w.lens[0]), n0
         toks = sum(L0 - n_0 + k + 1 for k in range(nrows))
         res["cpu_baseline"] = {"value": round(4 * w.D * w.Hq * toks / dt / 1e12, 6), "unit": "TFLOP/s",
-                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "cores": oracle.num_threads(), "cpu": cpu_model(),
+                               "kind": "oracle",
                                "sample": f"first {nrows} query rows of sequence 0, all heads",
                                "seconds": round(dt, 2)}
     print(json.dumps(res), flush=True)
@@ -544,6 +559,34 @@ def main():
                 "p10_us": round(float(np.percentile(c, 10)) * 1e3, 2),
                 "p90_us": round(float(np.percentile(c, 90)) * 1e3, 2),
                 "gbs_median": round(kv / (float(np.median(c)) * 1e-3) / 1e9, 2)}
+    # the same step captured once in a HIP graph (both kernels) and replayed:
+    # one host launch per step instead of two
+    graph = None
+    if args.graph:
+        gstream = torch.cuda.Stream(dev)
+        run_all = binding.prepare(*args_, stages=0, **{**kw, "stream": gstream})
+        run_all()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            run_all()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            gev[i][0].record(stream)
+            g.replay()
+            gev[i][1].record(stream)
+        torch.cuda.synchronize()
+        g_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        g_gpu = np.array([e[0].elapsed_time(e[1]) for e in gev])
+        graph = {"ms_per_step": round(g_step_ms, 5),
+                 "value": round(kv / (g_step_ms * 1e-3) / 1e9, 2),
+                 "gpu_us_median": round(float(np.median(g_gpu)) * 1e3, 2)}
+        del g
+
     esz = w.esz
     n_blocks = int(((w.lens + w.B - 1) // w.B).sum())
     alg_total = kv + 2 * w.S * w.Hq * w.D * esz + 4 * n_blocks + 4 * w.S
@@ -574,6 +617,7 @@ def main():
                       "partitions_p90": round(float(np.percentile(part_ms, 90)) * 1e3, 2),
                       "combine": round(float(comb_ms.mean()) * 1e3, 2)},
         "cold_cache": cold,
+        "graph": graph,
         "alg_bytes_total": alg_total,
         "workspace_bytes": plan["workspace_bytes"],
         "flops_alg": int(w.lens.sum()) * w.Hq * 4 * w.D,
