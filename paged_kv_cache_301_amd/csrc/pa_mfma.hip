@@ -105,23 +105,24 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
         constexpr int kIter = 32 * W;          // tokens per iteration
         const int niter = (t_end - t_begin + kIter - 1) / kIter;
         const int tw = t_begin + 32 * w;       // this wave's sub-tile of iteration 0
-        KVTile ta, tb;
-        ctx.load(ta, tw);
-        // The scheduling barriers keep each prefetch ahead of the wait for
-        // the tile computed next; without them the compiler sinks the loads
-        // below that wait and the wave never has two tiles in flight.
-        for (int it = 0; it < niter; it += 2) {
+        // One sub-tile of registers: as soon as this wave's sub-tile is in
+        // LDS its registers take the loads of the next one, which stay in
+        // flight through the barrier and both products.  (Holding two
+        // register tiles and prefetching before the compute needs 223 VGPRs
+        // instead of 184 and was 1-4 % slower.)  The scheduling barriers keep
+        // the compiler from sinking that prefetch below the products.
+        KVTile tile;
+        ctx.load(tile, tw);
+        for (int it = 0; it < niter; ++it) {
             const int t0 = t_begin + kIter * it;
-            ctx.load(tb, tw + kIter * (it + 1));
+            mfma_stage(tile, klds[w], vlds[w], g, i);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_compute<T, W>(st, ta, qf, klds, vlds, w, t0, t_end, t_end, t_end, g, i, a.scale_log2);
+            if (it + 1 < niter) ctx.load(tile, tw + kIter * (it + 1));   // uniform
             __builtin_amdgcn_sched_barrier(0);
-            ctx.load(ta, tw + kIter * (it + 2));
-            __builtin_amdgcn_sched_barrier(0);
-            if (it + 1 < niter)
-                mfma_compute<T, W>(st, tb, qf, klds, vlds, w, t0 + kIter, t_end, t_end, t_end, g, i,
-                                   a.scale_log2);
-            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();   // every wave's rows visible
+            const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
+            mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, t_end, g, i, a.scale_log2);
+            __syncthreads();   // reads done before the next stage overwrites LDS
         }
         st.l += shfl_xor(st.l, 16);
         st.l += shfl_xor(st.l, 32);

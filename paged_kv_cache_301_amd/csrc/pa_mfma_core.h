@@ -218,21 +218,5 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
     st.l += ps;
 }
 
-// One iteration: every wave stages its sub-tile, then all W sub-tiles that
-// start before t_end (the partition end) are consumed together.  t0 = first
-// token of the iteration; lim / t_full as in mfma_tiles.
-template <typename T, int W, bool PER_COLUMN = false>
-__device__ __forceinline__ void mfma_compute(MfmaState<T> &st, const KVTile &tile,
-                                             const typename Mfma<T>::Vec (&qf)[4],
-                                             uint4 (*klds)[32 * 16], uint4 (*vlds)[32 * 16],
-                                             int w, int t0, int t_end, int lim, int t_full,
-                                             int g, int i, float scale_log2) {
-    mfma_stage(tile, klds[w], vlds[w], g, i);
-    __syncthreads();   // rows visible to every lane of every wave
-    const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-    mfma_tiles<T, W, PER_COLUMN>(st, qf, klds, vlds, t0, nsub, lim, t_full, g, i, scale_log2);
-    __syncthreads();   // reads done before the next iteration overwrites LDS
-}
-
 }  // namespace mfma
 }  // namespace pa
