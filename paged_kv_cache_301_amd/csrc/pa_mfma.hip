@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();   // every wave's rows visible
             const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-            mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, t_end, g, i, a.scale_log2);
+            mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, a.scale_log2);
             __syncthreads();   // reads done before the next stage overwrites LDS
         }
         st.l += shfl_xor(st.l, 16);

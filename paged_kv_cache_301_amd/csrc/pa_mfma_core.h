@@ -118,16 +118,13 @@ __device__ __forceinline__ void mfma_stage(const KVTile &tile, uint4 *klds, uint
 // first nsub (wave-uniform, 1 <= nsub <= NS) are inside the partition.  All
 // score products are issued before the softmax and all P.V products after
 // it, so the matrix core has independent work while the vector unit waits,
-// and one maximum / rescale step serves all NS sub-tiles.  Token t counts for
-// this lane's column iff t < lim; t_full (wave-uniform, <= every column's
-// lim) marks sub-tiles that need no mask.  Decode: lim = t_full = the
-// partition end, and t0 < lim.  With PER_COLUMN, a column may have seen no
-// valid token yet (its running max is still -inf) and its weights are then
-// forced to 0.
-template <typename T, int NS, bool PER_COLUMN = false>
+// and one maximum / rescale step serves all NS sub-tiles.  Tokens at or past
+// t_end (the partition end, wave-uniform; t0 < t_end) are masked; sub-tiles
+// that end before it need no mask.
+template <typename T, int NS>
 __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma<T>::Vec (&qf)[4],
                                            const uint4 (*klds)[32 * 16], const uint4 (*vlds)[32 * 16],
-                                           int t0, int nsub, int lim, int t_full, int g, int i,
+                                           int t0, int nsub, int t_end, int g, int i,
                                            float scale_log2) {
     using M = Mfma<T>;
     using Vec = typename M::Vec;
@@ -153,13 +150,13 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
         if (u >= nsub) {                              // uniform: past the partition
 #pragma unroll
             for (int j = 0; j < 8; ++j) x[u][j] = kNegInf;
-        } else if (tu + 32 <= t_full) {               // uniform: counts for every column
+        } else if (tu + 32 <= t_end) {                // uniform: no token masked
 #pragma unroll
             for (int j = 0; j < 8; ++j) x[u][j] = acc[u][j >> 2][j & 3] * scale_log2;
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                x[u][j] = (tu + 16 * (j >> 2) + 4 * g + (j & 3) < lim)
+                x[u][j] = (tu + 16 * (j >> 2) + 4 * g + (j & 3) < t_end)
                               ? acc[u][j >> 2][j & 3] * scale_log2 : kNegInf;
         }
     }
@@ -187,8 +184,8 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
         for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
         st.m = mn;
     }
-    // a column with no valid token so far keeps m = -inf: its weights are 0
-    const float mref = (PER_COLUMN && st.m == kNegInf) ? 0.f : st.m;
+    // st.m is finite here: the first sub-tile (t0 < t_end) has a valid token
+    const float mref = st.m;
 
     const int row_a = 4 * g + (i >> 2);
     const int sw = swz_v(row_a);
