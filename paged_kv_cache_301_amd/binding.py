@@ -141,6 +141,15 @@ def _check(status: int):
 
 
 def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False) -> PaConfig:
+    """The C config.  Choices left to the library (kernel "auto", partition 0)
+    take the PA_KERNEL (auto / generic / valu / mfma) and PA_PARTITION_TOKENS
+    environment variables when those are set; explicit arguments win."""
+    if isinstance(kernel, str) and kernel == "auto":
+        kernel = os.environ.get("PA_KERNEL", "auto") or "auto"
+    if not partition_tokens:
+        partition_tokens = int(os.environ.get("PA_PARTITION_TOKENS", "0") or 0)
+    if isinstance(kernel, str) and kernel not in KERNELS:
+        raise ValueError(f"unknown kernel {kernel!r} (one of {sorted(KERNELS)})")
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
     return PaConfig(k, int(partition_tokens), int(stages), int(bool(kv_reuse)))
 

@@ -131,6 +131,21 @@ def test_kv_write_validation(lib):
     assert lib.pa_append_kv(None, None, None, None, None, None, 0, 2, 8, 4, 4, 3, F16, None) == b.PA_OK
 
 
+def test_environment_overrides(monkeypatch):
+    """PA_KERNEL / PA_PARTITION_TOKENS fill in the choices a call leaves to
+    the library; explicit arguments win."""
+    args = (64, 32, 8, 128, 16, 15360, 256, torch.bfloat16)
+    assert b.plan(*args)["kernel"] == b.KERNEL_MFMA
+    monkeypatch.setenv("PA_KERNEL", "generic")
+    monkeypatch.setenv("PA_PARTITION_TOKENS", "256")
+    assert b.plan(*args)["kernel"] == b.KERNEL_GENERIC
+    assert b.plan(*args, kernel="mfma")["partition_tokens"] == 256
+    assert b.plan(*args, kernel="mfma", partition_tokens=512)["partition_tokens"] == 512
+    monkeypatch.setenv("PA_KERNEL", "nonsense")
+    with pytest.raises(ValueError):
+        b.plan(*args)
+
+
 def test_read_bytes_validation(lib):
     fake = 1 << 20
     assert lib.pa_read_bytes(None, 0, None, None) == b.PA_OK
