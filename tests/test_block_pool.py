@@ -328,3 +328,60 @@ def test_serving_loop_with_forks_matches_oracle():
     assert torch.equal(dk.cpu().view(torch.uint8), kc.view(torch.uint8))
     assert torch.equal(dv.cpu().view(torch.uint8), vc.view(torch.uint8))
     assert pool.num_free == len(ref.free)
+
+
+def test_library_pool_concurrent_threads():
+    """Eight host threads drive one pool at once (each on its own sequences;
+    the C calls run without the interpreter lock).  Afterwards every count
+    agrees with the tables: a block's reference count is the number of live
+    tables holding it, the free count is the number of unreferenced blocks,
+    and every sequence has the length its thread gave it."""
+    import threading
+
+    NB, B = 16384, 16
+    pool = b.BlockPool(NB, B)
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            rng = random.Random(tid)
+            mine = {}
+            for _ in range(400):
+                op = rng.random()
+                if op < 0.2 or not mine:
+                    mine[pool.create()] = 0
+                elif op < 0.75:
+                    sid = rng.choice(list(mine))
+                    n = rng.randint(1, 40)
+                    slots, _ = pool.append(sid, n)
+                    assert len(slots) == n
+                    mine[sid] += n
+                elif op < 0.9:
+                    parent = rng.choice(list(mine))
+                    mine[pool.fork(parent)] = mine[parent]
+                else:
+                    sid = rng.choice(list(mine))
+                    pool.release(sid)
+                    del mine[sid]
+            results[tid] = mine
+        except Exception as e:  # reported below, in the main thread
+            errors.append((tid, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    live = {sid: n for mine in results.values() for sid, n in mine.items()}
+    counts = np.zeros(NB, dtype=np.int64)
+    maxb = max(pool.num_blocks_of(s) for s in live)
+    tables, lens = pool.export(list(live), maxb, pad=-1)
+    for row, sid, n in zip(tables.tolist(), live, lens.tolist()):
+        assert n == live[sid] == pool.length(sid)
+        used = [x for x in row if x >= 0]
+        assert len(used) == -(-n // B)
+        for x in used:
+            counts[x] += 1
+    assert [pool.refcount(x) for x in range(NB)] == counts.tolist()
+    assert pool.num_free == int((counts == 0).sum())
