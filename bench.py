@@ -10,6 +10,14 @@ logical token, once per (sequence, kv head)), plus the dominant kernel's
 roofline figures (HIP events on the launch stream) and the CPU oracle timed
 on the host as a baseline.
 
+Timing.  The K timed steps run back to back with nothing else on the stream:
+the wall clock between two synchronisations gives ms_per_step, and one HIP
+event pair around the whole loop gives the GPU time per step.  An event
+recorded between two launches costs about 4 us of GPU time (measured: three
+per step turned 360 us into 371 on mha_7b and 22 into 33 on mha_small), so
+no event is recorded inside the loop.  Kernel durations come the same way
+from K back-to-back launches of that kernel alone, between one event pair.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mha_7b]
 """
 from __future__ import annotations
@@ -28,6 +36,24 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense matrix-core peaks
 METRIC = "Paged decode attention: achieved KV-read GB/s and % of HBM peak; seqs/s"
 KERNEL_NAMES = {0: "auto", 1: "generic", 2: "valu", 3: "mfma"}
+
+
+def time_loop(fn, n, stream):
+    """Run fn() n times back to back; returns (wall ms per call, GPU ms per
+    call from one event pair around the loop).  Synchronises before and
+    after."""
+    import torch
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / n, e0.elapsed_time(e1) / n
 
 
 def parse():
@@ -266,18 +292,8 @@ def bench_write(args, w, dev):
     alg_bytes = 2 * row_bytes + meta_bytes           # read once, write once
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e in evs:
-        e[0].record(stream)
-        step()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    step_ms = wall * 1e3 / args.steps
+    # one launch per step: the loop's event pair gives the kernel's average
+    step_ms, k_ms = time_loop(step, args.steps, stream)
     gbs = alg_bytes / (step_ms * 1e-3) / 1e9
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
     kernel = "pa_copy_blocks" if args.op == "copy_blocks" else "pa_kv_write"
@@ -371,29 +387,22 @@ def bench_prefill(args, dev):
               partition_tokens=args.partition_tokens, workspace=ws, stream=stream)
     a = (pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, pw.query_start, w.scale, out)
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
+    def parts():
         binding.prefill(*a, stages=binding.STAGE_PARTITIONS, **kw)
-        if evs is not None:
-            evs[1].record(stream)
+
+    def combine():
+        binding.prefill(*a, stages=binding.STAGE_COMBINE, **kw)
+
+    def step():
+        parts()
         if plan["split"]:
-            binding.prefill(*a, stages=binding.STAGE_COMBINE, **kw)
-        if evs is not None:
-            evs[2].record(stream)
+            combine()
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    c_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    step_ms = wall * 1e3 / args.steps
+    step_ms, _ = time_loop(step, args.steps, stream)
+    _, k_ms = time_loop(parts, args.steps, stream)
+    c_ms = time_loop(combine, args.steps, stream)[1] if plan["split"] else 0.0
     flops = pw.flops()
     tf = flops / (step_ms * 1e-3) / 1e12
     achieved = flops / (k_ms * 1e-3) / 1e12
@@ -508,39 +517,26 @@ def main():
     run_parts = binding.prepare(*args_, stages=binding.STAGE_PARTITIONS, **kw)
     run_combine = binding.prepare(*args_, stages=binding.STAGE_COMBINE, **kw)
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
+    def step():
         run_parts()
-        if evs is not None:
-            evs[1].record(stream)
         if plan["split"]:
             run_combine()
-        if evs is not None:
-            evs[2].record(stream)
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    comb_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    step_ms = wall * 1e3 / args.steps
+    step_ms, step_gpu_ms = time_loop(step, args.steps, stream)
+    # kernel durations: each kernel alone, launched back to back
+    _, part_ms = time_loop(run_parts, args.steps, stream)
+    comb_ms = time_loop(run_combine, args.steps, stream)[1] if plan["split"] else 0.0
 
     kv = w.kv_bytes()
     gbs = kv / (step_ms * 1e-3) / 1e9
-    part_avg = float(part_ms.mean())
+    part_avg = float(part_ms)
     achieved = kv / (part_avg * 1e-3) / 1e9
     kname = KERNEL_NAMES[plan["kernel"]]
-    print(f"[bench] plan {plan}; partition kernel avg {part_avg * 1e3:.1f} us "
-          f"(min {part_ms.min() * 1e3:.1f}), combine avg {comb_ms.mean() * 1e3:.1f} us, "
-          f"step {step_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    print(f"[bench] plan {plan}; partition kernel avg {part_avg * 1e3:.1f} us, "
+          f"combine avg {comb_ms * 1e3:.1f} us, step {step_ms * 1e3:.1f} us "
+          f"(GPU {step_gpu_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
 
     # cold cache: the same step after a 1 GiB scratch write (outside the events)
     cold = None
@@ -549,10 +545,12 @@ def main():
         cold_ms = []
         for i in range(args.cold_calls):
             scratch.fill_(i & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            step(e)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            step()
+            e[1].record(stream)
             torch.cuda.synchronize()
-            cold_ms.append(e[0].elapsed_time(e[2]))
+            cold_ms.append(e[0].elapsed_time(e[1]))
         del scratch
         c = np.array(cold_ms)
         cold = {"calls": args.cold_calls, "median_us": round(float(np.median(c)) * 1e3, 2),
@@ -573,18 +571,10 @@ def main():
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
-        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            gev[i][0].record(stream)
-            g.replay()
-            gev[i][1].record(stream)
-        torch.cuda.synchronize()
-        g_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        g_gpu = np.array([e[0].elapsed_time(e[1]) for e in gev])
+        g_step_ms, g_gpu_ms = time_loop(g.replay, args.steps, stream)
         graph = {"ms_per_step": round(g_step_ms, 5),
                  "value": round(kv / (g_step_ms * 1e-3) / 1e9, 2),
-                 "gpu_us_median": round(float(np.median(g_gpu)) * 1e3, 2)}
+                 "gpu_us": round(g_gpu_ms * 1e3, 2)}
         del g
 
     esz = w.esz
@@ -612,10 +602,9 @@ def main():
                    "split": bool(plan["split"])},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),
+        "step_gpu_us": round(step_gpu_ms * 1e3, 2),
         "kernel_us": {"partitions": round(part_avg * 1e3, 2),
-                      "partitions_p10": round(float(np.percentile(part_ms, 10)) * 1e3, 2),
-                      "partitions_p90": round(float(np.percentile(part_ms, 90)) * 1e3, 2),
-                      "combine": round(float(comb_ms.mean()) * 1e3, 2)},
+                      "combine": round(float(comb_ms) * 1e3, 2)},
         "cold_cache": cold,
         "graph": graph,
         "alg_bytes_total": alg_total,
