@@ -333,3 +333,20 @@ def test_check_inputs_reports_bad_tables_and_lengths():
                          w.scale, out_dtype=torch.float32, check=True)
     torch.cuda.synchronize()
     check(out, oracle_full(w), torch.bfloat16, "checked decode")
+
+
+# ------------------------------------------------ the small config, every row
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_small_config_every_row(dt):
+    """The 8-sequence, 32/32-head, B = 16 configuration (lengths U[1, 2048])
+    compared on every output row: in fp32 (the plain kernel; max-abs 1e-5)
+    and in its own fp16 (automatic plan, split contexts; rel 2e-3 with fp32
+    output, plus the final rounding in fp16)."""
+    say(f"case: small config every row, {dt}")
+    w = workloads.make_workload("mha_small", device=DEV, poison=True, dtype=dt)
+    ref = oracle_full(w)
+    out = run(w, out_dtype=torch.float32)
+    check(out, ref, DT[dt], f"mha_small/{dt}")
+    if dt != "f32":
+        check(run(w), ref, DT[dt], f"mha_small/{dt}/native")
