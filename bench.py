@@ -578,6 +578,7 @@ def main():
         del g
 
     esz = w.esz
+    unique = w.unique_kv_bytes() if w.spec.prefix_tokens else None
     n_blocks = int(((w.lens + w.B - 1) // w.B).sum())
     alg_total = kv + 2 * w.S * w.Hq * w.D * esz + 4 * n_blocks + 4 * w.S
 
@@ -596,12 +597,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "B": w.B, "tokens": int(w.lens.sum()), "kv_bytes": kv,
-                   "unique_kv_bytes": w.unique_kv_bytes() if w.spec.prefix_tokens else kv,
+                   "unique_kv_bytes": unique or kv,
                    "kernel": kname, "partition_tokens": plan["partition_tokens"],
                    "kv_reuse": kv_reuse,
                    "split": bool(plan["split"])},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),
+        # with a prefix shared by the batch, the rate on the bytes stored once
+        # (each shared block counted once): the conservative figure
+        "unique_gbs": round(unique / (step_ms * 1e-3) / 1e9, 2) if unique else None,
+        "unique_hbm_frac": round(unique / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                           if unique else None,
         "step_gpu_us": round(step_gpu_ms * 1e3, 2),
         "kernel_us": {"partitions": round(part_avg * 1e3, 2),
                       "combine": round(float(comb_ms) * 1e3, 2)},
