@@ -168,7 +168,11 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         ctx.load(ta, t_begin);
         // The scheduling barriers keep each prefetch ahead of the wait for
         // the tile computed next; without them the compiler sinks the loads
-        // below that wait and the wave never has two tiles in flight.
+        // below that wait and the wave never has two tiles in flight.  The
+        // loads past the partition's last tile are left unconditional (they
+        // re-read rows just read, see TileLoader): guarding them raised the
+        // kernel from 159 to 206 VGPRs, two waves per SIMD instead of three,
+        // and was slower.
         for (int it = 0; it < niter; it += 2) {
             const int t0 = t_begin + 32 * it;
             ctx.load(tb, t0 + 32);
