@@ -65,6 +65,9 @@ def parse():
                     help="mha_small | mha_7b | gqa_70b | gqa_long | mqa (default: mha_7b, the batch-64 case)")
     ap.add_argument("--block-size", type=int, default=None, help="override B (gqa_long sweeps 1/8/16/32)")
     ap.add_argument("--q-heads", type=int, default=None, help="override Hq (e.g. mqa with 32 query heads)")
+    ap.add_argument("--seqs", type=int, default=None, help="override the number of sequences S")
+    ap.add_argument("--fixed-len", type=int, default=None,
+                    help="every sequence this many tokens (a uniform batch; the table fits it)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--kv-reuse", choices=["on", "off"], default="off",
@@ -141,6 +144,10 @@ def record_key(workload: str, args) -> str:
     key = workload
     if args.q_heads:
         key += f"_hq{args.q_heads}"
+    if getattr(args, "seqs", None):
+        key += f"_s{args.seqs}"
+    if getattr(args, "fixed_len", None):
+        key += f"_len{args.fixed_len}"
     if args.op == "prefill" and args.new_tokens:
         key += f"_new{args.new_tokens}"
     return key
@@ -491,6 +498,12 @@ def main():
         over["B"] = args.block_size
     if args.q_heads:
         over["Hq"] = args.q_heads
+    if args.seqs:
+        over["S"] = args.seqs
+    if args.fixed_len:
+        S = args.seqs or workloads.SPECS[args.workload].S
+        over["lens"] = ("fixed", (args.fixed_len,) * S)
+        over["max_len"] = args.fixed_len
     t_gen = time.perf_counter()
     w = workloads.make_workload(args.workload, device=dev, poison=False, **over)
     torch.cuda.synchronize()
@@ -599,7 +612,7 @@ def main():
                    "B": w.B, "tokens": int(w.lens.sum()), "kv_bytes": kv,
                    "unique_kv_bytes": unique or kv,
                    "kernel": kname, "partition_tokens": plan["partition_tokens"],
-                   "kv_reuse": kv_reuse,
+                   "kv_reuse": kv_reuse, "fixed_len": args.fixed_len,
                    "split": bool(plan["split"])},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),
