@@ -77,14 +77,18 @@ __device__ __forceinline__ void split_probs(const float (&p)[8], Vec &hi, Vec &l
 // group g therefore addresses row 4g + q / 4 (the second read: 16 rows
 // further), elements 16n + 4 (q % 4) .. +3, and receives V[4g + r][16n + q]
 // (second read: V[16 + 4g + r][16n + q]) for r = 0..3: exactly the A-operand
-// slots k = (g, r) and (g, 4 + r).  swz_v(r) = 2 ((r / 2) % 8) spreads the 16
-// rows one such read touches over 8 even chunk offsets, so its 64 eight-byte
-// accesses fill all 64 banks twice (the minimum for 512 bytes).
+// slots k = (g, r) and (g, 4 + r).  The four lanes of a row read 32
+// contiguous bytes (one chunk pair), and the LDS serves the read half a wave
+// (eight rows, 256 bytes) per cycle, so the eight rows of each half-wave must
+// land on eight different chunk pairs: swz_v(r) = 2 (r % 8).  (The earlier
+// 2 ((r / 2) % 8) gave two rows of each half-wave the same pair: rocprofv3
+// counted 2 bank-conflict cycles in every 4 of these reads.)  Rows r and
+// r + 16 share the swizzle, so the second read uses the same chunk offset.
 //
 // The 16-byte row writes of both images are conflict free (each row is a
 // permutation of its 16 chunks).
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
-__device__ __forceinline__ int swz_v(int row) { return 2 * ((row >> 1) & 7); }
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 7); }
 
 using i16x4 = short __attribute__((ext_vector_type(4)));
 using lds_i16x4 = __attribute__((address_space(3))) i16x4;
