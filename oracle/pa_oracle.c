@@ -86,32 +86,15 @@ static double load_elem(const void *base, size_t i, int dtype)
 }
 
 /*
- * One output row: query row qrow (query[qrow][h]) attending the first n
- * tokens of sequence s, query head h.  Writes D doubles to o.  Decode calls it
- * with qrow = s and n = seq_lens[s].  Returns ORACLE_ENOMEM if the gather
- * buffers cannot be allocated.
+ * Step 1 (gather): copy the first n tokens of sequence s, kv head g, from the
+ * paged pools into contiguous [n][D] matrices K and V, walking the logical
+ * blocks in order and cutting the last, partly filled one at n.
  */
-static int attend_row(const void *query, const void *key_cache,
-                      const void *value_cache, const int32_t *block_tables,
-                      int qrow, int n, double scale, double *o,
-                      int s, int h, int Hq, int Hkv, int D, int B,
+static void gather_kv(const void *key_cache, const void *value_cache,
+                      const int32_t *block_tables, int s, int g, int n,
+                      double *K, double *V, int Hkv, int D, int B,
                       int max_blocks, int dtype)
 {
-    int G = Hq / Hkv;
-    int g = h / G;                   /* kv head shared by this query head */
-
-    for (int d = 0; d < D; ++d) o[d] = 0.0;
-    if (n <= 0) return ORACLE_OK;
-
-    /* Step 1: gather K and V into contiguous [n][D] matrices. */
-    double *K = malloc(sizeof(double) * (size_t)n * D);
-    double *V = malloc(sizeof(double) * (size_t)n * D);
-    double *x = malloc(sizeof(double) * (size_t)n);
-    double *qv = malloc(sizeof(double) * (size_t)D);
-    if (!K || !V || !x || !qv) {
-        free(K); free(V); free(x); free(qv);
-        return ORACLE_ENOMEM;
-    }
     int nblocks = (n + B - 1) / B;
     int t = 0;
     for (int j = 0; j < nblocks; ++j) {
@@ -125,6 +108,24 @@ static int attend_row(const void *query, const void *key_cache,
                 V[(size_t)t * D + d] = load_elem(value_cache, base + d, dtype);
             }
         }
+    }
+}
+
+/*
+ * Steps 2-4 (standard attention on contiguous K / V): query row qrow, head h
+ * against the first n >= 1 rows of K and V.  Writes D doubles to o.  Returns
+ * ORACLE_ENOMEM if a scratch buffer cannot be allocated.
+ */
+static int attend_gathered(const void *query, const double *K, const double *V,
+                           int qrow, int n, double scale, double *o,
+                           int h, int Hq, int D, int dtype)
+{
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    double *x = malloc(sizeof(double) * (size_t)n);
+    double *qv = malloc(sizeof(double) * (size_t)D);
+    if (!x || !qv) {
+        free(x); free(qv);
+        return ORACLE_ENOMEM;
     }
 
     /* Step 2: scores x_t = scale * q . K_t. */
@@ -147,8 +148,39 @@ static int attend_row(const void *query, const void *key_cache,
     for (int tt = 0; tt < n; ++tt)
         for (int d = 0; d < D; ++d) o[d] += x[tt] * V[(size_t)tt * D + d];
 
-    free(K); free(V); free(x); free(qv);
+    free(x); free(qv);
     return ORACLE_OK;
+}
+
+/*
+ * One output row: query row qrow (query[qrow][h]) attending the first n
+ * tokens of sequence s, query head h (gather, then standard attention).
+ * Writes D doubles to o.  Decode calls it with qrow = s and n = seq_lens[s].
+ * Returns ORACLE_ENOMEM if the gather buffers cannot be allocated.
+ */
+static int attend_row(const void *query, const void *key_cache,
+                      const void *value_cache, const int32_t *block_tables,
+                      int qrow, int n, double scale, double *o,
+                      int s, int h, int Hq, int Hkv, int D, int B,
+                      int max_blocks, int dtype)
+{
+    int G = Hq / Hkv;
+    int g = h / G;                   /* kv head shared by this query head */
+
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (n <= 0) return ORACLE_OK;
+
+    double *K = malloc(sizeof(double) * (size_t)n * D);
+    double *V = malloc(sizeof(double) * (size_t)n * D);
+    if (!K || !V) {
+        free(K); free(V);
+        return ORACLE_ENOMEM;
+    }
+    gather_kv(key_cache, value_cache, block_tables, s, g, n, K, V, Hkv, D, B,
+              max_blocks, dtype);
+    int rc = attend_gathered(query, K, V, qrow, n, scale, o, h, Hq, D, dtype);
+    free(K); free(V);
+    return rc;
 }
 
 /*
@@ -253,8 +285,21 @@ int oracle_prefill(const void *query, const void *key_cache,
         if (row < 0 || row >= T * Hq) return ORACLE_EINVAL;
     }
 
-    int status = ORACLE_OK;
-#pragma omp parallel for schedule(dynamic, 1)
+    /* The requested rows, bucketed by (sequence, kv head): each bucket's
+     * sequence is gathered once (all L_s tokens), and every row attends its
+     * own prefix of that gather.  Tokens 0 .. pos of a logical-order gather
+     * are exactly a gather of pos + 1 tokens, so each row's arithmetic is
+     * the same as gathering for that row alone. */
+    int G = Hq / Hkv;
+    int nb = S * Hkv;
+    int *count = calloc((size_t)nb + 1, sizeof(int));
+    int *order = malloc(sizeof(int) * (size_t)(nrows > 0 ? nrows : 1));
+    int *seq_of = malloc(sizeof(int) * (size_t)(nrows > 0 ? nrows : 1));
+    int *pos_of = malloc(sizeof(int) * (size_t)(nrows > 0 ? nrows : 1));
+    if (!count || !order || !seq_of || !pos_of) {
+        free(count); free(order); free(seq_of); free(pos_of);
+        return ORACLE_ENOMEM;
+    }
     for (int r = 0; r < nrows; ++r) {
         int row = rows ? rows[r] : r;
         int t = row / Hq, h = row % Hq;
@@ -262,14 +307,56 @@ int oracle_prefill(const void *query, const void *key_cache,
         while (query_start[s + 1] <= t) ++s;
         int n = query_start[s + 1] - query_start[s];
         int pos = seq_lens[s] - n + (t - query_start[s]);
-        int rc = attend_row(query, key_cache, value_cache, block_tables,
-                            t, pos + 1, scale, out + (size_t)r * D,
-                            s, h, Hq, Hkv, D, B, max_blocks, dtype);
-        if (rc != ORACLE_OK) {
-#pragma omp atomic write
-            status = rc;
-        }
+        seq_of[r] = s;
+        pos_of[r] = pos;
+        count[s * Hkv + h / G + 1] += 1;
     }
+    for (int k = 0; k < nb; ++k) count[k + 1] += count[k];
+    {
+        int *fill = malloc(sizeof(int) * (size_t)(nb > 0 ? nb : 1));
+        if (!fill) {
+            free(count); free(order); free(seq_of); free(pos_of);
+            return ORACLE_ENOMEM;
+        }
+        for (int k = 0; k < nb; ++k) fill[k] = count[k];
+        for (int r = 0; r < nrows; ++r) {
+            int row = rows ? rows[r] : r;
+            order[fill[seq_of[r] * Hkv + (row % Hq) / G]++] = r;
+        }
+        free(fill);
+    }
+
+    int status = ORACLE_OK;
+    for (int k = 0; k < nb && status == ORACLE_OK; ++k) {
+        int lo = count[k], hi = count[k + 1];
+        if (lo == hi) continue;
+        int s = k / Hkv, g = k % Hkv;
+        int L = seq_lens[s];              /* >= 1: the sequence has query rows */
+        double *K = malloc(sizeof(double) * (size_t)L * D);
+        double *V = malloc(sizeof(double) * (size_t)L * D);
+        if (!K || !V) {
+            free(K); free(V);
+            status = ORACLE_ENOMEM;
+            break;
+        }
+        gather_kv(key_cache, value_cache, block_tables, s, g, L, K, V, Hkv, D, B,
+                  max_blocks, dtype);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int i = lo; i < hi; ++i) {
+            int r = order[i];
+            int row = rows ? rows[r] : r;
+            int t = row / Hq, h = row % Hq;
+            int pos = pos_of[r];
+            int rc = attend_gathered(query, K, V, t, pos + 1, scale, out + (size_t)r * D,
+                                     h, Hq, D, dtype);
+            if (rc != ORACLE_OK) {
+#pragma omp atomic write
+                status = rc;
+            }
+        }
+        free(K); free(V);
+    }
+    free(count); free(order); free(seq_of); free(pos_of);
     return status;
 }
 
