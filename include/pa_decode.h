@@ -3,9 +3,11 @@
  *
  * C ABI of libpa_decode.so.  Every pointer argument named *_cache, query,
  * block_tables, seq_lens, out or workspace is a DEVICE pointer owned by the
- * caller; the library allocates nothing, keeps no device state between calls
- * and never synchronises the stream.  All compute entry points are
- * asynchronous on `stream` (a hipStream_t; NULL is the default stream).
+ * caller; the library allocates nothing.  All compute entry points are
+ * asynchronous on `stream` (a hipStream_t; NULL is the default stream) and
+ * never synchronise it, except in the checked mode described at
+ * pa_get_device_error.  The only device state the library keeps is the small
+ * per-device word of that checked mode.
  *
  * The operation (pages "Paged Attention > The PagedAttention Algorithm",
  * sections "Standard Attention vs PagedAttention" and "Optimized CUDA
@@ -32,9 +34,15 @@
  *     seq_lens     [S]               int32
  *     out          [S][Hq][D]        element type `out_dtype`
  *
- * Preconditions on device data (the caller guarantees them; they are not
- * checked): 0 <= seq_lens[s] <= max_blocks * B, and
- * 0 <= block_tables[s][j] < NB for every j < ceil(seq_lens[s] / B).
+ * Preconditions on device data (the caller guarantees them; the attention
+ * kernels do not check them): 0 <= seq_lens[s] <= max_blocks * B, and
+ * 0 <= block_tables[s][j] < NB for every j < ceil(seq_lens[s] / B).  In the
+ * checked mode (PA_CHECK=1 in the environment, or pa_config.check = 1) the
+ * library verifies them on the device before any attention kernel runs and
+ * returns PA_ERR_DEVICE_CHECK instead of launching ("PagedAttention by
+ * hand", section "Forward pass", Step 2: slots past a sequence's context may
+ * hold whatever an earlier sequence left there, so lengths and table entries
+ * decide what may be read).
  *
  * Arithmetic: fp32 accumulation for fp16 / bf16 inputs; the output is rounded
  * to `out_dtype` (round to nearest even) once, at the end.
@@ -53,16 +61,23 @@ extern "C" {
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
 /* Status codes.  Every entry point validates its host-side arguments before
- * launching anything; on a non-OK status nothing was launched. */
+ * launching anything: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED and
+ * PA_ERR_WORKSPACE mean nothing was launched, and so does
+ * PA_ERR_DEVICE_CHECK.  PA_ERR_HIP means a launch failed; a kernel queued
+ * earlier in the same call (e.g. the partition pass before a failing
+ * combine) may still run. */
 typedef enum {
     PA_OK = 0,
     PA_ERR_NULL = 1,        /* a required pointer is NULL                       */
-    PA_ERR_SHAPE = 2,       /* negative / zero size, Hq % Hkv != 0, size overflow */
+    PA_ERR_SHAPE = 2,       /* negative / zero size, Hq % Hkv != 0, size overflow,
+                               or a launch grid beyond the hardware limits       */
     PA_ERR_UNSUPPORTED = 3, /* dtype, head size or kernel choice not supported  */
     PA_ERR_WORKSPACE = 4,   /* workspace missing, too small or misaligned       */
-    PA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch      */
+    PA_ERR_HIP = 5,         /* the HIP runtime reported an error                */
     PA_ERR_NO_BLOCKS = 6,   /* block pool: not enough free blocks (nothing changed) */
-    PA_ERR_BAD_ID = 7       /* block pool: unknown or released sequence / block id */
+    PA_ERR_BAD_ID = 7,      /* block pool: unknown or released sequence / block id */
+    PA_ERR_DEVICE_CHECK = 8 /* checked mode: a length or used table entry breaks
+                               the preconditions; no attention kernel ran       */
 } pa_status;
 
 /* Kernel families (pa_config.kernel). */
@@ -102,6 +117,9 @@ typedef struct {
                              the batch share blocks (a common prompt prefix),
                              so repeated rows can hit in L2 / Infinity Cache.
                              Results are identical either way.                  */
+    int check;            /* checked mode: 0 follows the PA_CHECK environment
+                             variable (on when it is "1"), 1 always checks,
+                             -1 never checks.  See pa_get_device_error.          */
 } pa_config;
 
 /* The plan a call will execute (filled by pa_decode_plan). */
@@ -145,7 +163,8 @@ size_t pa_decode_workspace_bytes(int S, int Hq, int Hkv, int D, int B, int NB,
  * S = 0 is a no-op returning PA_OK.
  *
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (e.g. D > 512,
- * out_dtype not in {dtype, PA_F32}), PA_ERR_WORKSPACE, PA_ERR_HIP.
+ * out_dtype not in {dtype, PA_F32}), PA_ERR_WORKSPACE, PA_ERR_HIP, and in the
+ * checked mode PA_ERR_DEVICE_CHECK.
  */
 pa_status pa_decode(const void *query, const void *key_cache,
                     const void *value_cache, const int32_t *block_tables,
@@ -208,7 +227,6 @@ pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_
                        int S, int Hkv, int D, int B, int NB, int max_blocks,
                        pa_dtype dtype, void *stream);
 
-/* Human-readable name of a status code (static storage). */
 /*
  * pa_copy_blocks -- batched whole-block copy inside both caches, the copy step
  * of copy-on-write (page "PagedAttention by hand", section "Memory Sharing
@@ -247,6 +265,31 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pair
 pa_status pa_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, int S,
                           int max_blocks, int B, int NB, int32_t *report, void *stream);
 
+/*
+ * pa_get_device_error -- the sticky result of the library's device input
+ * check on the current device (the device `stream` belongs to).
+ *
+ * Checked mode.  When PA_CHECK=1 is set in the environment (read at every
+ * call) or pa_config.check = 1, pa_decode, pa_decode_ex and pa_prefill first
+ * run the device check of pa_check_inputs (lengths within the table, every
+ * used table entry within the pool; for pa_prefill also query_start ordered,
+ * from 0 to T, with 0 <= n_s <= min(seq_lens[s], max_query_len)) on
+ * `stream`, wait for it (the call synchronises `stream`, so the checked mode
+ * cannot be captured in a HIP graph) and, if any sequence fails, return
+ * PA_ERR_DEVICE_CHECK without launching an attention kernel: `out` and the
+ * workspace are left untouched.  A failing check also sets a per-device
+ * error word that stays set until read here.
+ *
+ * This call synchronises `stream`, returns PA_ERR_DEVICE_CHECK if the word
+ * is set (and clears it), PA_OK otherwise, PA_ERR_HIP on a runtime error.
+ * `first_bad` may be NULL; otherwise it receives the smallest offending
+ * sequence index of the device's most recent check if the word is set and
+ * that check failed, else -1.  Checks on one device share the word: calls
+ * that overlap on several streams of one device race for it.
+ */
+pa_status pa_get_device_error(void *stream, int32_t *first_bad);
+
+/* Human-readable name of a status code (static storage). */
 const char *pa_status_string(pa_status status);
 
 #ifdef __cplusplus

@@ -27,7 +27,8 @@
  *     query_start  [S+1]           int32, device
  *     out          [T][Hq][D]      element type `out_dtype`
  *
- * Device-data preconditions (not checked): query_start[0] = 0, non-decreasing,
+ * Device-data preconditions (the kernels do not check them; the checked mode
+ * of pa_decode.h does, before launching): query_start[0] = 0, non-decreasing,
  * query_start[S] = T; 0 <= n_s <= max_query_len; n_s <= L_s <= max_blocks * B
  * when n_s > 0; valid block ids for the first ceil(L_s / B) table entries.
  *
@@ -38,8 +39,9 @@
  * pa_prefill_plan reports (256-byte aligned device memory).
  *
  * Errors: PA_ERR_NULL, PA_ERR_SHAPE (also T > 65535 or S > 65535),
- * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP.  T = 0 or S = 0 is a
- * no-op.  Asynchronous on `stream`; nothing is allocated.
+ * PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, and in the checked mode
+ * PA_ERR_DEVICE_CHECK.  T = 0 or S = 0 is a no-op.  Asynchronous on `stream`
+ * (the checked mode synchronises it); nothing is allocated.
  */
 #ifndef PA_PREFILL_H
 #define PA_PREFILL_H

@@ -24,7 +24,7 @@ HEADER = os.path.join(INCLUDE, "pa_decode.h")
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 # pa_status
 (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
- PA_ERR_NO_BLOCKS, PA_ERR_BAD_ID) = range(8)
+ PA_ERR_NO_BLOCKS, PA_ERR_BAD_ID, PA_ERR_DEVICE_CHECK) = range(9)
 # pa_kernel
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA = range(4)
 KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA}
@@ -36,7 +36,7 @@ _TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA
 
 class PaConfig(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("partition_tokens", ctypes.c_int),
-                ("stages", ctypes.c_int), ("kv_reuse", ctypes.c_int)]
+                ("stages", ctypes.c_int), ("kv_reuse", ctypes.c_int), ("check", ctypes.c_int)]
 
 
 class PaPlan(ctypes.Structure):
@@ -92,6 +92,8 @@ def load():
                                [ctypes.POINTER(PaConfig), _PTR, ctypes.c_size_t, _PTR])
     lib.pa_check_inputs.restype = _INT
     lib.pa_check_inputs.argtypes = [_PTR, _PTR] + [_INT] * 4 + [_PTR, _PTR]
+    lib.pa_get_device_error.restype = _INT
+    lib.pa_get_device_error.argtypes = [_PTR, ctypes.POINTER(ctypes.c_int32)]
     lib.pa_copy_blocks.restype = _INT
     lib.pa_copy_blocks.argtypes = [_PTR] * 3 + [_INT] * 6 + [_PTR]
     lib.pa_read_bytes.restype = _INT
@@ -135,12 +137,25 @@ def status_string(status: int) -> str:
     return load().pa_status_string(status).decode()
 
 
+class InputCheckError(PaError, ValueError):
+    """The library's device check found lengths or block-table entries that
+    violate the documented preconditions; nothing was launched."""
+
+
 def _check(status: int):
+    if status == PA_ERR_DEVICE_CHECK:
+        raise InputCheckError(status, status_string(status))
     if status != PA_OK:
         raise PaError(status, status_string(status))
 
 
-def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False) -> PaConfig:
+def _check_flag(check) -> int:
+    """pa_config.check: None leaves it to the PA_CHECK environment variable
+    (read by the library at every call), True / False force it."""
+    return 0 if check is None else (1 if check else -1)
+
+
+def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, check=None) -> PaConfig:
     """The C config.  Choices left to the library (kernel "auto", partition 0)
     take the PA_KERNEL (auto / generic / valu / mfma) and PA_PARTITION_TOKENS
     environment variables when those are set; explicit arguments win."""
@@ -151,7 +166,7 @@ def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False) -> PaCo
     if isinstance(kernel, str) and kernel not in KERNELS:
         raise ValueError(f"unknown kernel {kernel!r} (one of {sorted(KERNELS)})")
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    return PaConfig(k, int(partition_tokens), int(stages), int(bool(kv_reuse)))
+    return PaConfig(k, int(partition_tokens), int(stages), int(bool(kv_reuse)), _check_flag(check))
 
 
 def _shape_args(query, key_cache, block_tables, out_dtype):
@@ -185,10 +200,12 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     [NB,Hkv,B,D], block_tables[S,max_blocks] int32 and seq_lens[S] int32.
 
     All tensors must be contiguous and on the same GPU.  Asynchronous on
-    ``stream`` (default: torch's current stream).  ``check`` (default: the
-    PA_CHECK=1 environment variable) first verifies the lengths and table
-    entries on the device and raises InputCheckError instead of launching
-    (this synchronises the stream).
+    ``stream`` (default: torch's current stream); ``out`` and the workspace,
+    when this function allocates them, are allocated on that stream.
+    ``check`` (default None: the library follows the PA_CHECK environment
+    variable) makes the library verify the lengths and table entries on the
+    device first; it raises InputCheckError instead of launching (the checked
+    call synchronises the stream).
     """
     lib = load()
     for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
@@ -205,26 +222,27 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
         raise ValueError("key_cache and value_cache shapes differ")
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else query.dtype
-    if out is None:
-        out = torch.empty(query.shape, dtype=out_dtype, device=query.device)
-    elif out.shape != query.shape or out.dtype != out_dtype or not out.is_contiguous():
+    if out is not None and (out.shape != query.shape or out.dtype != out_dtype
+                            or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [S,Hq,D] tensor of out_dtype")
     shape = _shape_args(query, key_cache, block_tables, out_dtype)
     if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
         raise ValueError("seq_lens / block_tables do not match the batch size")
-    if _checking(check):
-        _run_check(block_tables, seq_lens, key_cache, stream)
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
+    tstream = _torch_stream(stream, query.device)
+    with torch.cuda.stream(tstream):
+        # allocated on the launch stream: the caching allocator then orders
+        # any reuse of these blocks after the kernels that use them
+        if out is None:
+            out = torch.empty(query.shape, dtype=out_dtype, device=query.device)
+        if p.workspace_bytes and workspace is None:
+            workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=query.device)
     ws_ptr, ws_bytes = None, 0
     if p.workspace_bytes:
-        if workspace is None:
-            workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=query.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(query.device)
-    st = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    st = tstream.cuda_stream
     _check(lib.pa_decode_ex(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
                             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
                             out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr, ws_bytes, st))
@@ -252,7 +270,8 @@ def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start, 
     paged K/V pools and block_tables / seq_lens (lengths count the new
     tokens).  ``max_query_len`` (the largest n_s) is read back from
     query_start when not given, which synchronises the stream.  ``check`` as
-    in ``decode``."""
+    in ``decode``; ``out`` and the workspace, when allocated here, are
+    allocated on the launch stream."""
     lib = load()
     for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
                     ("block_tables", block_tables), ("seq_lens", seq_lens),
@@ -279,26 +298,27 @@ def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start, 
         max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if S else 0
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else query.dtype
-    if out is None:
-        out = torch.empty(query.shape, dtype=out_dtype, device=query.device)
-    elif out.shape != query.shape or out.dtype != out_dtype or not out.is_contiguous():
+    if out is not None and (out.shape != query.shape or out.dtype != out_dtype
+                            or not out.is_contiguous()):
         raise ValueError("out must be a contiguous [T,Hq,D] tensor of out_dtype")
     shape = (S, T, Hq, Hkv, D, B, NB, block_tables.shape[1], int(max_query_len),
              _TORCH_TO_PA[query.dtype], _TORCH_TO_PA[out_dtype])
-    if _checking(check):
-        _run_check(block_tables, seq_lens, key_cache, stream)
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
     p = PaPlan()
     _check(lib.pa_prefill_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
+    tstream = _torch_stream(stream, query.device)
+    with torch.cuda.stream(tstream):
+        if out is None:
+            out = torch.empty(query.shape, dtype=out_dtype, device=query.device)
+        if p.workspace_bytes and workspace is None:
+            workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=query.device)
     ws_ptr, ws_bytes = None, 0
     if p.workspace_bytes:
-        if workspace is None:
-            workspace = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=query.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.pa_prefill(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
                           block_tables.data_ptr(), seq_lens.data_ptr(), query_start.data_ptr(),
                           float(scale), out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr,
-                          ws_bytes, _stream_handle(stream, query.device)))
+                          ws_bytes, tstream.cuda_stream))
     return out
 
 
@@ -307,10 +327,6 @@ def prefill_workload(pw, **kw) -> torch.Tensor:
     w = pw.base
     return prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
                    pw.query_start, w.scale, max_query_len=pw.max_query_len, **kw)
-
-
-class InputCheckError(ValueError):
-    """Lengths or block-table entries violate the documented preconditions."""
 
 
 def check_inputs(block_tables, seq_lens, num_blocks: int, block_size: int, stream=None):
@@ -336,17 +352,25 @@ def check_inputs(block_tables, seq_lens, num_blocks: int, block_size: int, strea
     return bad, (first if bad else None)
 
 
-def _checking(check) -> bool:
-    return bool(check) if check is not None else os.environ.get("PA_CHECK", "0") == "1"
+def device_error(stream=None):
+    """The library's sticky device-check result on the stream's device:
+    (status, smallest offending sequence or None).  Reading clears it;
+    synchronises the stream."""
+    first = ctypes.c_int32(-1)
+    st = load().pa_get_device_error(_stream_handle(stream, None), ctypes.byref(first))
+    if st not in (PA_OK, PA_ERR_DEVICE_CHECK):
+        _check(st)
+    return st, (first.value if first.value >= 0 else None)
 
 
-def _run_check(block_tables, seq_lens, key_cache, stream):
-    NB, _, B, _ = key_cache.shape
-    bad, first = check_inputs(block_tables, seq_lens, NB, B, stream)
-    if bad:
-        raise InputCheckError(
-            f"{bad} sequence(s) violate the length / block-table preconditions "
-            f"(first: sequence {first}); nothing was launched")
+def _torch_stream(stream, device):
+    """A torch stream object for ``stream`` (None: the current stream of
+    ``device``; a raw hipStream_t handle is wrapped as an external stream)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def _stream_handle(stream, device):
@@ -531,14 +555,12 @@ class PreparedCall:
 def prepare(query, key_cache, value_cache, block_tables, seq_lens, scale, out, *,
             kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, workspace=None,
             stream=None, check: Optional[bool] = None) -> PreparedCall:
-    """Validate once (by running the same checks as ``decode`` on a plan, and
-    with ``check`` the device check of the current lengths and tables) and
-    return a PreparedCall that launches the configured stage(s)."""
+    """Validate once (by running the same checks as ``decode`` on a plan) and
+    return a PreparedCall that launches the configured stage(s).  ``check``
+    as in ``decode``: the library's device check then runs at every call."""
     lib = load()
     shape = _shape_args(query, key_cache, block_tables, out.dtype)
-    if _checking(check):
-        _run_check(block_tables, seq_lens, key_cache, stream)
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
     if p.workspace_bytes and workspace is None:

@@ -5,6 +5,7 @@
 // (and are tested) on machines without a GPU.
 #include <climits>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "pa_internal.h"
@@ -100,6 +101,23 @@ long long table_cap(int kernel, int B) {
     return staged ? 1024LL * B : (long long)INT_MAX;
 }
 
+// Threads per work-group of a decode kernel family (the matrix-core kernel
+// runs ceil(G / 16) waves).
+int decode_threads(int kernel, int G) {
+    return kernel == PA_KERNEL_MFMA ? 64 * ((G + 15) / 16) : 64;
+}
+
+// Grid of the tiled decode kernels: 1 = the 1-D live-item grid (every
+// work-group decodes its item from the lengths one wave holds, pa_sched.h),
+// 0 = the rectangular (sequence x kv head, partition) grid, -1 = neither
+// fits the launch limits.
+int decode_grid_mode(int S, int Hkv, int parts, int threads) {
+    const long long pairs = (long long)S * Hkv;
+    if (S <= pa::kSchedMaxSeqs && pa::grid_fits(pairs * parts, threads)) return 1;
+    if (pa::grid_fits(pairs, threads) && parts <= pa::kMaxPartitions) return 0;
+    return -1;
+}
+
 pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
                     pa_dtype dtype, pa_dtype out_dtype, const pa_config *cfg, pa_plan *plan) {
     pa_status st = validate_shape(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype);
@@ -157,11 +175,14 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
         }
     }
     if (kernel == PA_KERNEL_GENERIC) {
-        // one pass over the whole context; no workspace
+        // one pass over the whole context; no workspace.  Grid (Hq, S) of
+        // 64-thread work-groups: within the limits for every valid shape.
         p.kernel = kernel;
         p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
         p.max_partitions = 1;
         p.split = 0;
+    } else if (decode_grid_mode(S, Hkv, p.max_partitions, decode_threads(kernel, Hq / Hkv)) < 0) {
+        return PA_ERR_SHAPE;
     }
     if (p.split) {
         const size_t rows = (size_t)S * Hq * p.max_partitions;
@@ -172,6 +193,15 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Checked mode: the config's explicit choice, else PA_CHECK=1 in the
+// environment (read at every call, so a process can switch it at run time).
+bool check_enabled(const pa_config *cfg) {
+    if (cfg && cfg->check > 0) return true;
+    if (cfg && cfg->check < 0) return false;
+    const char *env = std::getenv("PA_CHECK");
+    return env && std::strcmp(env, "1") == 0;
+}
 
 // ---------------------------------------------------------------- multi-token
 
@@ -216,7 +246,10 @@ pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB,
         const int qpb = pa::kPrefillColumns / (Hq / Hkv);
         const long long qb = (max_query_len + qpb - 1) / qpb;
         const long long groups = qb * S * Hkv;
-        if ((groups + 8 * qb) >= (1LL << 31)) return PA_ERR_SHAPE;   // grid x, padded to whole XCD rounds
+        // grid x: the (sequence, kv head) pairs padded to whole XCD rounds,
+        // times the query blocks, of kPrefillThreads threads each
+        const long long grid_x = ((long long)S * Hkv + 7) / 8 * 8 * qb;
+        if (!pa::grid_fits(grid_x, pa::kPrefillThreads)) return PA_ERR_SHAPE;
         long long part;
         if (req > 0) {
             part = req;
@@ -289,11 +322,22 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     if (plan.kernel != PA_KERNEL_GENERIC &&
         !(aligned16(query) && aligned16(key_cache) && aligned16(value_cache) && aligned16(out))) {
         if (cfg && cfg->kernel != PA_KERNEL_AUTO) return PA_ERR_UNSUPPORTED;
-        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0, 0};
+        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0, 0, cfg ? cfg->check : 0};
         st = make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, &gen, &plan);
         if (st != PA_OK) return st;
     }
     const int stages = (cfg && cfg->stages) ? cfg->stages : PA_STAGE_ALL;
+    if (plan.split && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+                       workspace_bytes < plan.workspace_bytes))
+        return PA_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (check_enabled(cfg)) {
+        int bad = 0;
+        if (pa::library_check(block_tables, seq_lens, nullptr, S, 0, 0, max_blocks, B, NB, hs,
+                              &bad) != hipSuccess)
+            return PA_ERR_HIP;
+        if (bad) return PA_ERR_DEVICE_CHECK;
+    }
 
     Args a;
     std::memset(&a, 0, sizeof a);
@@ -317,12 +361,12 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     a.split = plan.split;
     a.stream_kv = (cfg && cfg->kv_reuse) ? 0 : 1;
     // live-item grid when every work-group can decode its item from the
-    // lengths held in one wave's registers, and the 1-D grid fits
-    a.compact = (S <= 1024 && (long long)S * Hkv * plan.max_partitions * 64 < (1LL << 32)) ? 1 : 0;
+    // lengths held in one wave's registers and the 1-D grid fits (the plan
+    // has checked that one of the two grids fits)
+    a.compact = plan.kernel != PA_KERNEL_GENERIC &&
+                decode_grid_mode(S, Hkv, plan.max_partitions,
+                                 decode_threads(plan.kernel, Hq / Hkv)) == 1;
     if (plan.split) {
-        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
-            workspace_bytes < plan.workspace_bytes)
-            return PA_ERR_WORKSPACE;
         const size_t rows = (size_t)S * Hq * plan.max_partitions;
         char *ws = static_cast<char *>(workspace);
         a.part_o = reinterpret_cast<float *>(ws);
@@ -331,7 +375,6 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
                                              align256(rows * sizeof(float)));
     }
 
-    hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t err = hipSuccess;
     if (stages & PA_STAGE_PARTITIONS) {
         switch (plan.kernel) {
@@ -375,12 +418,23 @@ pa_status pa_prefill(const void *query, const void *key_cache, const void *value
     if (plan.kernel != PA_KERNEL_GENERIC &&
         !(aligned16(query) && aligned16(key_cache) && aligned16(value_cache) && aligned16(out))) {
         if (cfg && cfg->kernel != PA_KERNEL_AUTO) return PA_ERR_UNSUPPORTED;
-        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0, 0};
+        pa_config gen{PA_KERNEL_GENERIC, 0, cfg ? cfg->stages : 0, 0, cfg ? cfg->check : 0};
         st = make_prefill_plan(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype, out_dtype,
                                &gen, &plan, &qb);
         if (st != PA_OK) return st;
     }
     const int stages = (cfg && cfg->stages) ? cfg->stages : PA_STAGE_ALL;
+    if (plan.split && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+                       workspace_bytes < plan.workspace_bytes))
+        return PA_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (check_enabled(cfg)) {
+        int bad = 0;
+        if (pa::library_check(block_tables, seq_lens, query_start, S, T, max_query_len, max_blocks,
+                              B, NB, hs, &bad) != hipSuccess)
+            return PA_ERR_HIP;
+        if (bad) return PA_ERR_DEVICE_CHECK;
+    }
 
     Args a;
     std::memset(&a, 0, sizeof a);
@@ -407,9 +461,6 @@ pa_status pa_prefill(const void *query, const void *key_cache, const void *value
     a.T = T;
     a.q_blocks = qb;
     if (plan.split) {
-        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
-            workspace_bytes < plan.workspace_bytes)
-            return PA_ERR_WORKSPACE;
         const size_t rows = (size_t)T * Hq * plan.max_partitions;
         char *ws = static_cast<char *>(workspace);
         a.part_o = reinterpret_cast<float *>(ws);
@@ -417,7 +468,6 @@ pa_status pa_prefill(const void *query, const void *key_cache, const void *value
         a.part_l = reinterpret_cast<float *>(ws + align256(rows * D * sizeof(float)) +
                                              align256(rows * sizeof(float)));
     }
-    hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t err = hipSuccess;
     if (stages & PA_STAGE_PARTITIONS) {
         err = plan.kernel == PA_KERNEL_MFMA ? pa::launch_prefill(a, dtype, out_dtype, hs)
@@ -446,6 +496,7 @@ pa_status pa_write_kv(const void *key, const void *value, const int32_t *slot_ma
                       void *key_cache, void *value_cache, int T, int Hkv, int D, int B, int NB,
                       pa_dtype dtype, void *stream) {
     if (T < 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0) return PA_ERR_SHAPE;
+    if (!pa::grid_fits(T, pa::kKvThreads)) return PA_ERR_SHAPE;            // grid x = token
     if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
     if (T == 0) return PA_OK;
     if (!key || !value || !slot_mapping || !key_cache || !value_cache) return PA_ERR_NULL;
@@ -460,6 +511,7 @@ pa_status pa_append_kv(const void *key, const void *value, const int32_t *block_
                        int Hkv, int D, int B, int NB, int max_blocks, pa_dtype dtype,
                        void *stream) {
     if (S < 0 || Hkv <= 0 || D <= 0 || B <= 0 || NB <= 0 || max_blocks < 0) return PA_ERR_SHAPE;
+    if (!pa::grid_fits(S, pa::kKvThreads)) return PA_ERR_SHAPE;            // grid x = sequence
     if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
     if (S == 0) return PA_OK;
     if (!key || !value || !block_tables || !seq_lens || !key_cache || !value_cache)
@@ -478,7 +530,10 @@ pa_status pa_copy_blocks(void *key_cache, void *value_cache, const int32_t *pair
     if (n == 0) return PA_OK;
     if (!key_cache || !value_cache || !pairs) return PA_ERR_NULL;
     const long long block_bytes = (long long)Hkv * B * D * dtype_size(dtype);
-    if (block_bytes > (1LL << 40)) return PA_ERR_SHAPE;
+    // grid x = pieces of one block
+    if (block_bytes > (1LL << 40) ||
+        !pa::grid_fits((block_bytes + pa::kCopyPieceBytes - 1) / pa::kCopyPieceBytes, pa::kKvThreads))
+        return PA_ERR_SHAPE;
     const hipError_t err = pa::launch_copy_blocks(key_cache, value_cache, pairs, n, block_bytes,
                                                   NB, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -492,6 +547,16 @@ pa_status pa_check_inputs(const int32_t *block_tables, const int32_t *seq_lens, 
     const hipError_t err = pa::launch_check(block_tables, seq_lens, S, max_blocks, B, NB, report,
                                             static_cast<hipStream_t>(stream));
     return err == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_get_device_error(void *stream, int32_t *first_bad) {
+    int set = 0, first = -1;
+    if (pa::read_device_error(static_cast<hipStream_t>(stream), &set, &first) != hipSuccess) {
+        if (first_bad) *first_bad = -1;
+        return PA_ERR_HIP;
+    }
+    if (first_bad) *first_bad = first;
+    return set ? PA_ERR_DEVICE_CHECK : PA_OK;
 }
 
 pa_status pa_read_bytes(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
@@ -512,6 +577,9 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the block pool has too few free blocks";
     case PA_ERR_BAD_ID: return "PA_ERR_BAD_ID: unknown or released sequence or block id";
+    case PA_ERR_DEVICE_CHECK:
+        return "PA_ERR_DEVICE_CHECK: a sequence length or used block-table entry breaks the "
+               "preconditions (checked mode); nothing was launched";
     }
     return "unknown pa_status";
 }

@@ -40,8 +40,19 @@ constexpr int kTileTokens = 32;
 // Partitions per (sequence, head): the partition index is grid dimension y.
 constexpr int kMaxPartitions = 65535;
 
+// Largest batch whose lengths one wave holds in registers for the live-item
+// decode of the tiled decode kernels (pa_sched.h); larger batches use the
+// rectangular grid.
+constexpr int kSchedMaxSeqs = 1024;
+
 // (query token, head) columns per work-group of the multi-token matrix-core
 // kernel: four waves of two 16-column groups.
 constexpr int kPrefillColumns = 128;
+constexpr int kPrefillThreads = 256;
+
+// Threads per work-group of the K / V write and block-copy kernels, and
+// bytes of one block one copy work-group moves.
+constexpr int kKvThreads = 256;
+constexpr int kCopyPieceBytes = kKvThreads * 16 * 2;
 
 }  // namespace pa

@@ -21,6 +21,21 @@ hipError_t launch_prefill(const Args &a, pa_dtype dt, pa_dtype odt, hipStream_t 
 hipError_t launch_check(const int32_t *block_tables, const int32_t *seq_lens, int S,
                         int max_blocks, int B, int NB, int32_t *report, hipStream_t st);
 
+// Checked mode: run the device check into the library's per-device state on
+// `st`, wait for it, and return the number of offending sequences in *bad
+// (query_start may be null: decode).
+hipError_t library_check(const int32_t *block_tables, const int32_t *seq_lens,
+                         const int32_t *query_start, int S, int T, int max_query_len,
+                         int max_blocks, int B, int NB, hipStream_t st, int *bad);
+// Synchronise `st`, read and clear the sticky error word of its device.
+hipError_t read_device_error(hipStream_t st, int *set, int *first_bad);
+
+// A 1-D launch of `groups` work-groups of `threads` threads fits the
+// hardware: grid.x <= 2^31 - 1 and grid.x * threads < 2^32.
+inline bool grid_fits(long long groups, long long threads) {
+    return groups >= 0 && groups <= 0x7fffffffLL && groups * threads < (1LL << 32);
+}
+
 hipError_t launch_kv_write(const void *key, const void *value, const int32_t *slot_mapping,
                            const int32_t *block_tables, const int32_t *seq_lens,
                            void *key_cache, void *value_cache, int T, int Hkv, int D, int B,

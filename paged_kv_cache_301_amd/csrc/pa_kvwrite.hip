@@ -32,7 +32,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kKvThreads;
 
 struct KvWriteArgs {
     const char *key;           // [T][Hkv][D]
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(kThreads) void kv_write_u16(KvWriteArgs a) {
 // multiple of 16 bytes and both caches are 16-byte aligned, else 2-byte units.
 constexpr int kCopyUnroll = 2;
 constexpr int kCopyPiece = kThreads * 16 * kCopyUnroll;
+static_assert(kCopyPiece == kCopyPieceBytes, "copy piece size");
 
 template <bool VEC16>
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char *kc, char *vc,

@@ -42,7 +42,7 @@ hipError_t launch_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_
     const size_t n = bytes / 16;
     const size_t per_block = (size_t)kReadThreads * kReadLoads;
     const size_t blocks = (n + per_block - 1) / per_block;
-    if (blocks > 0xFFFFFFFFull) return hipErrorInvalidValue;
+    if (!grid_fits((long long)blocks, kReadThreads)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, st,
                        static_cast<const uint4 *>(buf), n, sink);
     return hipGetLastError();

@@ -27,11 +27,11 @@
 // part 2 by a binary search over token counts, and the sequence with ballots.
 #pragma once
 
+#include "pa_args.h"
 #include "pa_device.h"
 
 namespace pa {
 
-constexpr int kSchedMaxSeqs = 1024;
 constexpr int kSchedChunks = kSchedMaxSeqs / 64;
 
 struct WorkItem {

@@ -26,8 +26,9 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(9):
         assert lib.pa_status_string(s).decode().startswith("PA_")
+    assert lib.pa_status_string(b.PA_ERR_DEVICE_CHECK).decode().startswith("PA_ERR_DEVICE_CHECK")
     assert b"unknown" in lib.pa_status_string(99)
 
 
@@ -163,3 +164,75 @@ def test_check_inputs_validation(lib):
     assert lib.pa_check_inputs(fake, fake, 2, 4, 16, 8, None, None) == b.PA_ERR_NULL
     assert lib.pa_check_inputs(fake, None, 2, 4, 16, 8, fake, None) == b.PA_ERR_NULL
     assert lib.pa_check_inputs(None, fake, 2, 4, 16, 8, fake, None) == b.PA_ERR_NULL
+
+
+# ------------------------------------------------------------ launch limits
+# A 1-D launch needs grid.x * threads < 2^32; shapes beyond it are rejected
+# by the planner (PA_ERR_SHAPE) instead of failing at launch.
+
+def _plan_status(S, Hq, Hkv, B=16, mb=4, kernel="auto", part=0):
+    p = b.PaPlan()
+    cfg = b.PaConfig(b.KERNELS[kernel], part, 0, 0, 0)
+    return b.load().pa_decode_plan(S, Hq, Hkv, 128, B, 100, mb, BF16, BF16,
+                                   ctypes.byref(cfg), ctypes.byref(p)), p
+
+
+def test_decode_grid_limit_counts_threads_per_work_group():
+    # 64 query heads per kv head: the matrix-core kernel runs 4 waves (256
+    # threads) per work-group; the rectangular grid is S * Hkv work-groups.
+    st, _ = _plan_status(65535, 64 * 256, 256)           # 65535 * 256 * 256 < 2^32
+    assert st == b.PA_OK
+    st, _ = _plan_status(65535, 64 * 257, 257)           # 65535 * 257 * 256 >= 2^32
+    assert st == b.PA_ERR_SHAPE
+    # one head per kv head: 64-thread work-groups (VALU kernel)
+    st, p = _plan_status(65535, 1024, 1024)              # 65535 * 1024 * 64 < 2^32
+    assert st == b.PA_OK and p.kernel == b.KERNEL_VALU
+    st, _ = _plan_status(65535, 1025, 1025)
+    assert st == b.PA_ERR_SHAPE
+    # the plain kernel's grid (Hq, S) always fits
+    st, p = _plan_status(65535, 1025, 1025, kernel="generic")
+    assert st == b.PA_OK and p.kernel == b.KERNEL_GENERIC
+    # a batch of at most 1024 sequences whose live-item grid would overflow
+    # falls back to the rectangular grid instead of failing
+    st, p = _plan_status(1024, 64, 1, mb=32768, kernel="mfma", part=32)
+    assert st == b.PA_OK and p.max_partitions == 16384
+    assert 1024 * 16384 * 256 >= 1 << 32
+
+
+def _prefill_status(S, T, Hq, Hkv, mql):
+    p = b.PaPlan()
+    return b.load().pa_prefill_plan(S, T, Hq, Hkv, 128, 16, 100, 8, mql, BF16, BF16, None,
+                                    ctypes.byref(p))
+
+
+def test_prefill_grid_limit_counts_threads_per_work_group():
+    # one head per kv head: 128 query tokens per 256-thread work-group, so
+    # max_query_len 65535 gives 512 query blocks per (sequence, kv head) pair,
+    # and the pairs are padded to a multiple of 8
+    assert _prefill_status(32760, 65535, 1, 1, 65535) == b.PA_OK        # 32760 * 512 < 2^24
+    assert _prefill_status(32761, 65535, 1, 1, 65535) == b.PA_ERR_SHAPE  # 32768 * 512 = 2^24
+    assert _prefill_status(65535, 65535, 1, 1, 65535) == b.PA_ERR_SHAPE
+
+
+def test_write_and_copy_grid_limits(lib):
+    fake = 1 << 20
+    # one 256-thread work-group per token / sequence: 2^24 of them overflow
+    assert lib.pa_write_kv(fake, fake, fake, fake, fake, 1 << 24, 2, 8, 4, 4, F16,
+                           None) == b.PA_ERR_SHAPE
+    assert lib.pa_append_kv(fake, fake, fake, fake, fake, fake, 1 << 24, 2, 8, 4, 4, 3, F16,
+                            None) == b.PA_ERR_SHAPE
+    # a block of 2^37 bytes is 2^24 copy pieces of 8 KiB
+    # (Hkv = 2^16, D = 2^12, B = 2^8, 2-byte elements)
+    assert lib.pa_copy_blocks(fake, fake, fake, 1, 1 << 16, 1 << 12, 1 << 8, 4, F16,
+                              None) == b.PA_ERR_SHAPE
+
+
+def test_checked_mode_follows_validation_order(lib, monkeypatch):
+    """Host-side errors come before the device check, which needs a GPU: with
+    PA_CHECK=1 an invalid call still returns its validation status, and the
+    S = 0 no-op stays a no-op."""
+    monkeypatch.setenv("PA_CHECK", "1")
+    assert _call(lib, Hq=6, Hkv=4) == b.PA_ERR_SHAPE
+    assert _call(lib, null=(0,)) == b.PA_ERR_NULL
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_AUTO, 32, 0, 0, 1)) == b.PA_ERR_WORKSPACE
+    assert _call(lib, S=0, null=(0, 1, 2, 3, 4, 5)) == b.PA_OK

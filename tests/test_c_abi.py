@@ -1,7 +1,10 @@
 """The ABI from plain C: the public headers are C99, and a C program with no
 Python or torch in its process drives every kernel family through
-pa_decode_plan / pa_decode_ex and checks the results against the oracle
-(tests/c_abi/decode_from_c.c, built by the package build step)."""
+pa_decode_plan / pa_decode_ex and checks the results against the oracle, then
+the checked mode (PA_CHECK=1 / pa_config.check): bad inputs are rejected with
+PA_ERR_DEVICE_CHECK before any attention kernel runs and pa_get_device_error
+reports them once (tests/c_abi/decode_from_c.c, built by the package build
+step)."""
 import os
 import subprocess
 
@@ -28,3 +31,5 @@ def test_decode_from_plain_c():
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.count(": max rel err") == 5 and "FAIL" not in r.stdout
+    # checked mode: rejected before any attention kernel, reported once
+    assert r.stdout.count(": ok") == 4

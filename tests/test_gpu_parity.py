@@ -1,9 +1,10 @@
 """GPU parity: the HIP library against the CPU oracle on identical seeded inputs.
 
-Small cases compare every output element; the benchmark-sized workloads
-compare sampled (sequence, head) rows, computed one by one by the oracle.
-Indexing is checked bit-exactly (needle, physical relabelling, NaN poison,
-run-to-run determinism).
+Every test compares every output element: small cases, and the
+benchmark-sized workloads at full size in the launch configuration the
+benchmark times.  Indexing is checked bit-exactly (needle, physical
+relabelling, NaN poison, run-to-run determinism, block ids repeated within a
+table).
 """
 import json
 import math
@@ -250,28 +251,27 @@ FULL = [("mha_small", {}), ("mha_7b", {}), ("gqa_70b", {}), ("gqa_long", {"B": 1
 
 
 @pytest.mark.parametrize("name,over", FULL)
-def test_full_size_sampled(name, over):
-    """Full-size workload, automatic plan (what the benchmark times); 48
-    sampled (sequence, head) rows against the oracle, plus finiteness of all."""
+def test_full_size_every_row(name, over):
+    """Full-size workload, automatic plan (what the benchmark times): every
+    (sequence, head) row against the oracle, with fp32 and with native
+    outputs.  The live-item grid decides which work-group computes which
+    (sequence, kv head, partition) item; a dropped or doubled item would
+    leave a row built from stale partial results, which only an all-row
+    comparison is sure to catch."""
     say(f"case: full-size {name} {over}")
     over = dict(over)
     kernel = over.pop("kernel", "auto")
     w = workloads.make_workload(name, device=DEV, poison=True, **over)
-    out = run(w, out_dtype=torch.float32, kernel=kernel)
-    assert torch.isfinite(out).all()
-    rng = np.random.default_rng(21)
-    rows = rng.choice(w.S * w.Hq, size=min(48, w.S * w.Hq), replace=False)
-    # always include the longest and the shortest sequence's first head
-    rows = sorted(set(rows.tolist()) | {int(np.argmax(w.lens)) * w.Hq,
-                                        int(np.argmin(w.lens)) * w.Hq + w.Hq - 1})
-    ref = oracle.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                        w.scale, rows=rows)
-    got = out.reshape(w.S * w.Hq, w.D)[torch.as_tensor(rows, device=DEV)]
-    check(got, ref, w.dtype, name)
-    # native-dtype output as well
-    out2 = run(w, kernel=kernel)
-    got2 = out2.reshape(w.S * w.Hq, w.D)[torch.as_tensor(rows, device=DEV)]
-    check(got2, ref, w.dtype, name + "/native")
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, kernel=kernel)
+    # workspace filled with NaN: any partial result the kernels do not
+    # rewrite poisons its row
+    ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+          if p["workspace_bytes"] else None)
+    out = run(w, out_dtype=torch.float32, kernel=kernel, workspace=ws)
+    ref = oracle_full(w)
+    say(f"  plan {p}; oracle done")
+    check(out, ref, w.dtype, name)
+    check(run(w, kernel=kernel, workspace=ws), ref, w.dtype, name + "/native")
 
 
 @pytest.mark.parametrize("kernel,Hq,Hkv,B", [("valu", 8, 8, 16), ("valu", 8, 8, 1), ("mfma", 16, 2, 16),
@@ -306,15 +306,32 @@ def test_many_sequences(kernel, Hq, Hkv, S):
 
 # ------------------------------------------------------- precondition check
 
-def test_check_inputs_reports_bad_tables_and_lengths():
+def _spare_pools(w, spare=16):
+    """The workload's pools copied into allocations with `spare` extra blocks
+    before and after the NB the calls see, returned as views of the middle NB
+    blocks: ids from -spare to NB + spare - 1 then stay inside the allocation
+    (the checked mode must reject them before any attention kernel reads
+    them)."""
+    big_k = torch.zeros((w.NB + 2 * spare,) + tuple(w.key_cache.shape[1:]), dtype=w.dtype,
+                        device=DEV)
+    big_v = torch.zeros_like(big_k)
+    big_k[spare:spare + w.NB] = w.key_cache
+    big_v[spare:spare + w.NB] = w.value_cache
+    return big_k[spare:spare + w.NB], big_v[spare:spare + w.NB]
+
+
+def test_check_inputs_reports_bad_tables_and_lengths(monkeypatch):
     """The device check counts exactly the sequences whose length or used
-    table entries break the preconditions; the binding refuses to launch on
-    them.  (No attention kernel ever sees the bad inputs.)"""
+    table entries break the preconditions.  In the checked mode the library
+    itself refuses to launch on them (PA_ERR_DEVICE_CHECK, raised as
+    InputCheckError), leaves the output untouched and reports the first bad
+    sequence once through pa_get_device_error."""
     say("case: device check of lengths and block tables")
     spec = workloads.WorkloadSpec("chk", S=6, Hq=8, Hkv=2, D=128, B=16, dtype="bf16",
                                   lens=("fixed", (0, 1, 16, 17, 100, 160)), max_len=160,
                                   pool=("free", 0.2), seed=41)
     w = workloads.make_workload(spec, device=DEV, poison=True)
+    kc, vc = _spare_pools(w)
     assert binding.check_inputs(w.block_tables, w.seq_lens, w.NB, w.B) == (0, None)
     bt = w.block_tables.clone()
     sl = w.seq_lens.clone()
@@ -327,12 +344,126 @@ def test_check_inputs_reports_bad_tables_and_lengths():
     sl2 = w.seq_lens.clone()
     sl2[0] = -3
     assert binding.check_inputs(w.block_tables, sl2, w.NB, w.B) == (1, 0)
+    assert binding.device_error() == (binding.PA_OK, None)
+    sentinel = torch.full(w.query.shape, 7.0, device=DEV)
+    out = sentinel.clone()
     with pytest.raises(binding.InputCheckError):
-        binding.decode(w.query, w.key_cache, w.value_cache, bt, sl, w.scale, check=True)
-    out = binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                         w.scale, out_dtype=torch.float32, check=True)
+        binding.decode(w.query, kc, vc, bt, sl, w.scale, out, check=True)
     torch.cuda.synchronize()
+    assert torch.equal(out, sentinel), "an attention kernel ran on rejected inputs"
+    assert binding.device_error() == (binding.PA_ERR_DEVICE_CHECK, 1)
+    assert binding.device_error() == (binding.PA_OK, None)
+    # the environment switch, read by the library at each call
+    monkeypatch.setenv("PA_CHECK", "1")
+    with pytest.raises(binding.InputCheckError):
+        binding.decode(w.query, kc, vc, w.block_tables, sl2, w.scale, out)
+    assert torch.equal(out, sentinel)
+    assert binding.device_error() == (binding.PA_ERR_DEVICE_CHECK, 0)
+    out = binding.decode(w.query, kc, vc, w.block_tables, w.seq_lens, w.scale,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert binding.device_error() == (binding.PA_OK, None)
     check(out, oracle_full(w), torch.bfloat16, "checked decode")
+    # an explicit check=False wins over the environment (good inputs only)
+    out = binding.decode(w.query, kc, vc, w.block_tables, w.seq_lens, w.scale,
+                         out_dtype=torch.float32, check=False)
+    torch.cuda.synchronize()
+    check(out, oracle_full(w), torch.bfloat16, "unchecked decode")
+
+
+def test_checked_prefill_rejects_bad_query_start():
+    """Multi-token calls in the checked mode also verify query_start (ordered,
+    0 .. T, each chunk within its sequence's length and max_query_len)."""
+    say("case: checked multi-token call, bad query_start / table")
+    spec = workloads.WorkloadSpec("chkq", S=3, Hq=8, Hkv=2, D=128, B=16, dtype="bf16",
+                                  lens=("fixed", (40, 100, 300)), max_len=320,
+                                  pool=("free", 0.2), seed=42)
+    pw = workloads.make_prefill_workload(spec, (5, 20, 7), device=DEV, poison=True)
+    w = pw.base
+    kc, vc = _spare_pools(w)
+    a = (pw.query, kc, vc, w.block_tables, w.seq_lens)
+    good = binding.prefill(*a, pw.query_start, w.scale, max_query_len=pw.max_query_len,
+                           out_dtype=torch.float32, check=True)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                         pw.query_start, w.scale)
+    check(good, ref, torch.bfloat16, "checked prefill")
+    qs = pw.query_start.clone()
+    qs[1] = qs[2] + 1                              # sequence 1 gets a negative row count
+    with pytest.raises(binding.InputCheckError):
+        binding.prefill(*a, qs, w.scale, max_query_len=pw.max_query_len, check=True)
+    assert binding.device_error() == (binding.PA_ERR_DEVICE_CHECK, 0)
+    with pytest.raises(binding.InputCheckError):   # a chunk longer than max_query_len
+        binding.prefill(*a, pw.query_start, w.scale, max_query_len=10, check=True)
+    assert binding.device_error()[0] == binding.PA_ERR_DEVICE_CHECK
+    bt = w.block_tables.clone()
+    bt[2, 3] = w.NB + 2                            # 300 tokens use entries 0 .. 18
+    with pytest.raises(binding.InputCheckError):
+        binding.prefill(pw.query, kc, vc, bt, w.seq_lens, pw.query_start, w.scale,
+                        max_query_len=pw.max_query_len, check=True)
+    assert binding.device_error() == (binding.PA_ERR_DEVICE_CHECK, 2)
+
+
+# ---------------------------------------------------- allocation and streams
+
+def test_side_stream_without_workspace():
+    """decode() on a side stream, with no workspace or output passed: both
+    are allocated on that stream, so memory freed afterwards and reused on
+    the current stream cannot be overwritten while the kernels still run."""
+    say("case: side stream, library-allocated workspace")
+    w = workloads.make_workload("mha_7b", device=DEV, poison=True, S=8,
+                                lens=("uniform", 2048, 4096), max_len=4096)
+    ref = oracle_full(w)
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    results = []
+    for trial in range(3):
+        out = binding.decode_workload(w, out_dtype=torch.float32, partition_tokens=256,
+                                      stream=side)
+        with torch.cuda.stream(side):
+            results.append(out.clone())
+        del out
+        # the current stream allocates and scribbles while the side stream runs
+        junk = [torch.full((1 << 20,), float("nan"), device=DEV) for _ in range(16)]
+        del junk
+    torch.cuda.synchronize()
+    for r in results:
+        check(r, ref, torch.bfloat16, "side stream")
+
+
+# ------------------------------------------------------ repeated block ids
+
+@pytest.mark.parametrize("kernel,Hq,Hkv,B", [("generic", 8, 2, 16), ("valu", 8, 8, 16),
+                                             ("valu", 8, 8, 1), ("mfma", 16, 2, 16),
+                                             ("mfma", 16, 4, 2), ("mfma", 64, 1, 16)])
+def test_repeated_block_ids_within_a_table(kernel, Hq, Hkv, B):
+    """One sequence's table names the same physical block at several logical
+    positions (the pages are silent on this; the oracle and the kernels read
+    tables without assuming distinct ids).  Every row against the oracle."""
+    say(f"case: repeated ids within a table {kernel} B={B}")
+    spec = workloads.WorkloadSpec("rep", S=4, Hq=Hq, Hkv=Hkv, D=128, B=B, dtype="bf16",
+                                  lens=("fixed", (37, 200, 513, 900)), max_len=900,
+                                  pool=("free", 0.3), seed=51)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    bt = w.block_tables.cpu().clone()
+    rng = np.random.default_rng(52)
+    for s, L in enumerate(w.lens):
+        n = (int(L) + B - 1) // B
+        n_full = int(L) // B     # blocks whose every slot holds a token (the last one's
+        if n_full == 0:          # tail is NaN in this poisoned pool)
+            continue
+        own = bt[s, :n_full].clone()
+        # every used entry drawn from a few of the sequence's own full blocks
+        pick = rng.choice(n_full, size=min(3, n_full), replace=False)
+        bt[s, :n] = own[torch.as_tensor(rng.choice(pick, size=n))]
+        assert len(set(bt[s, :n].tolist())) < n
+    bt = bt.to(DEV)
+    out = binding.decode(w.query, w.key_cache, w.value_cache, bt, w.seq_lens, w.scale,
+                         out_dtype=torch.float32, kernel=kernel,
+                         partition_tokens=64 if kernel != "generic" else 0)
+    torch.cuda.synchronize()
+    ref = oracle.decode(w.query, w.key_cache, w.value_cache, bt, w.seq_lens, w.scale)
+    check(out, ref, torch.bfloat16, f"repeated ids {kernel}")
 
 
 # ------------------------------------------------ the small config, every row
