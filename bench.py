@@ -5,18 +5,21 @@ every query head): the context-partition kernel, then the combine kernel when
 the plan splits contexts.  Inputs are synthetic and resident in HBM before
 timing starts.
 
-Prints one JSON line: whole-step KV-read throughput (GB/s of K+V bytes of every
-logical token, once per (sequence, kv head)), plus the dominant kernel's
-roofline figures (HIP events on the launch stream) and the CPU oracle timed
-on the host as a baseline.
+Prints one JSON line: KV-read throughput (GB/s of K+V bytes of every logical
+token, once per (sequence, kv head)) of the median cold-cache step, plus the
+dominant kernel's roofline figures (HIP events on the launch stream), the
+warm back-to-back rate, the other decode configurations measured the same
+way in the same process, and the CPU oracle timed on the host as a baseline.
 
-Timing.  The K timed steps run back to back with nothing else on the stream:
-the wall clock between two synchronisations gives ms_per_step, and one HIP
-event pair around the whole loop gives the GPU time per step.  An event
-recorded between two launches costs about 4 us of GPU time (measured: three
-per step turned 360 us into 371 on mha_7b and 22 into 33 on mha_small), so
-no event is recorded inside the loop.  Kernel durations come the same way
-from K back-to-back launches of that kernel alone, between one event pair.
+Timing.  Each of the K timed steps runs on a cold cache: a 1 GiB scratch
+write before it (outside its events) evicts the L2s and the 256 MB
+last-level cache, so every K / V byte comes from HBM.  One HIP event pair on
+the launch stream brackets each step; ms_per_step is their median and
+`value` the KV bytes over it.  The kernel durations come the same way, each
+kernel launched alone between one event pair after an eviction.  The warm
+figure runs K steps back to back between one event pair (an event recorded
+between two launches costs about 4 us of GPU time, so none is recorded
+inside that loop).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload mha_7b]
 """
@@ -77,9 +80,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-peak", action="store_true",
                     help="decode: skip the plain 4 GiB device read used as the measured HBM peak")
-    ap.add_argument("--cold-calls", type=int, default=20,
-                    help="decode: extra calls timed after writing a 1 GiB scratch buffer "
-                         "(evicts the L2s and the last-level cache); 0 to skip")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="decode: skip the other decode configurations (C2 mha_small, C4 "
+                         "gqa_70b, C5 gqa_long at B = 16) measured after the headline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--print-source-sha", action="store_true",
@@ -196,6 +199,94 @@ def measured_read_peak(dev, calls=5):
     med = float(np.median(ms))
     return {"gbs": round(nbytes / (med * 1e-3) / 1e9, 2), "bytes": nbytes,
             "kernel": "pa_read_bytes over a 4 GiB buffer", "calls": calls}
+
+
+def evict_and_time(fn, n, stream, scratch):
+    """n calls of fn(), each after a write of `scratch` (outside the events)
+    and bracketed by one HIP event pair on `stream`; returns the per-call
+    durations in ms."""
+    import torch
+    torch.cuda.synchronize()
+    pairs = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def stats_us(ms):
+    import numpy as np
+    a = np.asarray(ms) * 1e3
+    return {"median_us": round(float(np.median(a)), 2), "mean_us": round(float(a.mean()), 2),
+            "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2)}
+
+
+def measure_decode(w, args, dev, scratch, kernel="auto", partition_tokens=0, kv_reuse=False):
+    """Cold-cache and warm timings of one decode workload (see the module
+    docstring).  Returns (plan, timing dict, prepared step callables)."""
+    import torch
+    from paged_kv_cache_301_amd import binding
+    plan = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype,
+                        kernel=kernel, partition_tokens=partition_tokens)
+    ws = None
+    if plan["workspace_bytes"]:
+        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
+    out = torch.empty_like(w.query)
+    stream = torch.cuda.current_stream(dev)
+    kw = dict(kernel=kernel, partition_tokens=partition_tokens, workspace=ws, stream=stream,
+              kv_reuse=kv_reuse)
+    args_ = (w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale, out)
+    run_parts = binding.prepare(*args_, stages=binding.STAGE_PARTITIONS, **kw)
+    run_combine = binding.prepare(*args_, stages=binding.STAGE_COMBINE, **kw)
+
+    def step():
+        run_parts()
+        if plan["split"]:
+            run_combine()
+
+    for _ in range(args.warmup):
+        step()
+    t = {}
+    # the timed region: K cold steps
+    cold = evict_and_time(step, args.steps, stream, scratch)
+    t["cold"] = stats_us(cold)
+    # each kernel alone, cold
+    t["partitions"] = stats_us(evict_and_time(run_parts, args.steps, stream, scratch))
+    t["combine"] = (stats_us(evict_and_time(run_combine, args.steps, stream, scratch))
+                    if plan["split"] else None)
+    # warm: K steps back to back, and the partition kernel alone back to back
+    warm_ms, warm_gpu_ms = time_loop(step, args.steps, stream)
+    t["warm"] = {"ms_per_step": round(warm_ms, 5), "gpu_us": round(warm_gpu_ms * 1e3, 2),
+                 "partitions_us": round(time_loop(run_parts, args.steps, stream)[1] * 1e3, 2)}
+    return plan, t, (step, args_, kw)
+
+
+def decode_summary(w, plan, t, kname):
+    """Rates of one measured decode workload: logical and unique bytes."""
+    kv = w.kv_bytes()
+    unique = w.unique_kv_bytes() if w.spec.prefix_tokens else kv
+    step_s = t["cold"]["median_us"] * 1e-6
+    k_s = t["partitions"]["mean_us"] * 1e-6
+    return {
+        "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "B": w.B,
+        "tokens": int(w.lens.sum()), "kv_bytes": kv, "unique_kv_bytes": unique,
+        "kernel": kname, "partition_tokens": plan["partition_tokens"], "split": bool(plan["split"]),
+        "step_cold_us": t["cold"], "kernel_cold_us": t["partitions"],
+        "combine_cold_us": t["combine"], "warm": t["warm"],
+        "gbs": round(kv / step_s / 1e9, 2), "hbm_frac": round(kv / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "unique_gbs": round(unique / step_s / 1e9, 2),
+        "unique_hbm_frac": round(unique / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_gbs": round(kv / k_s / 1e9, 2),
+        "kernel_unique_hbm_frac": round(unique / k_s / 1e9 / HBM_PEAK_GBS, 4),
+        "seqs_per_s": round(w.S / step_s, 1),
+    }
 
 
 def cpu_model() -> str:
@@ -516,64 +607,28 @@ def main():
         bench_write(args, w, dev)
         return
 
-    plan = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype,
-                        kernel=args.kernel, partition_tokens=args.partition_tokens)
-    ws = None
-    if plan["workspace_bytes"]:
-        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
-    out = torch.empty_like(w.query)
-    stream = torch.cuda.current_stream(dev)
     kv_reuse = args.kv_reuse == "on"
-    kw = dict(kernel=args.kernel, partition_tokens=args.partition_tokens, workspace=ws,
-              stream=stream, kv_reuse=kv_reuse)
-    args_ = (w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale, out)
-    run_parts = binding.prepare(*args_, stages=binding.STAGE_PARTITIONS, **kw)
-    run_combine = binding.prepare(*args_, stages=binding.STAGE_COMBINE, **kw)
-
-    def step():
-        run_parts()
-        if plan["split"]:
-            run_combine()
-
-    for _ in range(args.warmup):
-        step()
-    step_ms, step_gpu_ms = time_loop(step, args.steps, stream)
-    # kernel durations: each kernel alone, launched back to back
-    _, part_ms = time_loop(run_parts, args.steps, stream)
-    comb_ms = time_loop(run_combine, args.steps, stream)[1] if plan["split"] else 0.0
-
-    kv = w.kv_bytes()
-    gbs = kv / (step_ms * 1e-3) / 1e9
-    part_avg = float(part_ms)
-    achieved = kv / (part_avg * 1e-3) / 1e9
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # cache eviction
+    plan, t, (step, args_, kw) = measure_decode(w, args, dev, scratch, kernel=args.kernel,
+                                                partition_tokens=args.partition_tokens,
+                                                kv_reuse=kv_reuse)
     kname = KERNEL_NAMES[plan["kernel"]]
-    print(f"[bench] plan {plan}; partition kernel avg {part_avg * 1e3:.1f} us, "
-          f"combine avg {comb_ms * 1e3:.1f} us, step {step_ms * 1e3:.1f} us "
-          f"(GPU {step_gpu_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
+    summ = decode_summary(w, plan, t, kname)
+    kv = w.kv_bytes()
+    step_ms = t["cold"]["median_us"] * 1e-3
+    gbs = kv / (step_ms * 1e-3) / 1e9
+    part_avg = t["partitions"]["mean_us"] * 1e-3
+    achieved = kv / (part_avg * 1e-3) / 1e9
+    print(f"[bench] plan {plan}; cold: step median {t['cold']['median_us']:.1f} us, partition "
+          f"kernel mean {t['partitions']['mean_us']:.1f} us, combine "
+          f"{(t['combine'] or {}).get('mean_us', 0.0):.1f} us; warm step "
+          f"{t['warm']['ms_per_step'] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
-    # cold cache: the same step after a 1 GiB scratch write (outside the events)
-    cold = None
-    if args.cold_calls > 0:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        cold_ms = []
-        for i in range(args.cold_calls):
-            scratch.fill_(i & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(stream)
-            step()
-            e[1].record(stream)
-            torch.cuda.synchronize()
-            cold_ms.append(e[0].elapsed_time(e[1]))
-        del scratch
-        c = np.array(cold_ms)
-        cold = {"calls": args.cold_calls, "median_us": round(float(np.median(c)) * 1e3, 2),
-                "p10_us": round(float(np.percentile(c, 10)) * 1e3, 2),
-                "p90_us": round(float(np.percentile(c, 90)) * 1e3, 2),
-                "gbs_median": round(kv / (float(np.median(c)) * 1e-3) / 1e9, 2)}
     # the same step captured once in a HIP graph (both kernels) and replayed:
     # one host launch per step instead of two
     graph = None
     if args.graph:
+        stream = kw["stream"]
         gstream = torch.cuda.Stream(dev)
         run_all = binding.prepare(*args_, stages=0, **{**kw, "stream": gstream})
         run_all()
@@ -590,8 +645,30 @@ def main():
                  "gpu_us": round(g_gpu_ms * 1e3, 2)}
         del g
 
+    # the other decode configurations, measured the same way (automatic plan)
+    extra = None
+    if not args.no_extra_configs and not (args.block_size or args.q_heads or args.seqs
+                                          or args.fixed_len or args.kernel != "auto"
+                                          or args.partition_tokens):
+        extra = {}
+        for key, name, over in (("mha_small", "mha_small", {}), ("gqa_70b", "gqa_70b", {}),
+                                ("gqa_long_B16", "gqa_long", {"B": 16})):
+            if name == args.workload and over.get("B", w.B) == w.B:
+                continue
+            wx = workloads.make_workload(name, device=dev, poison=False, **over)
+            torch.cuda.synchronize()
+            px, tx, _ = measure_decode(wx, args, dev, scratch, kv_reuse=kv_reuse)
+            extra[key] = decode_summary(wx, px, tx, KERNEL_NAMES[px["kernel"]])
+            e = extra[key]
+            print(f"[bench] {key}: cold step {e['step_cold_us']['median_us']:.1f} us "
+                  f"({e['gbs']:.0f} GB/s logical, {e['unique_hbm_frac'] * 100:.1f} % of 8 TB/s "
+                  f"on unique bytes), kernel {e['kernel_cold_us']['mean_us']:.1f} us",
+                  file=sys.stderr, flush=True)
+            del wx
+    del scratch
+
     esz = w.esz
-    unique = w.unique_kv_bytes() if w.spec.prefix_tokens else None
+    unique = summ["unique_kv_bytes"] if w.spec.prefix_tokens else None
     n_blocks = int(((w.lens + w.B - 1) // w.B).sum())
     alg_total = kv + 2 * w.S * w.Hq * w.D * esz + 4 * n_blocks + 4 * w.S
 
@@ -613,7 +690,7 @@ def main():
                    "unique_kv_bytes": unique or kv,
                    "kernel": kname, "partition_tokens": plan["partition_tokens"],
                    "kv_reuse": kv_reuse, "fixed_len": args.fixed_len,
-                   "split": bool(plan["split"])},
+                   "split": bool(plan["split"]), "timing": "cold cache, median step"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),
         # with a prefix shared by the batch, the rate on the bytes stored once
@@ -621,10 +698,9 @@ def main():
         "unique_gbs": round(unique / (step_ms * 1e-3) / 1e9, 2) if unique else None,
         "unique_hbm_frac": round(unique / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                            if unique else None,
-        "step_gpu_us": round(step_gpu_ms * 1e3, 2),
-        "kernel_us": {"partitions": round(part_avg * 1e3, 2),
-                      "combine": round(float(comb_ms) * 1e3, 2)},
-        "cold_cache": cold,
+        "step_cold_us": t["cold"],
+        "kernel_us": {"partitions": t["partitions"], "combine": t["combine"]},
+        "warm": {**t["warm"], "value": round(kv / (t["warm"]["ms_per_step"] * 1e-3) / 1e9, 2)},
         "graph": graph,
         "alg_bytes_total": alg_total,
         "workspace_bytes": plan["workspace_bytes"],
@@ -634,6 +710,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"pa_{kname}_partitions", record_key(args.workload, args), w.B,
                                                  plan["partition_tokens"])},
+        "configs": extra,
     }
     if not args.no_read_peak:
         peak = measured_read_peak(dev)
