@@ -76,8 +76,10 @@ typedef enum {
     PA_ERR_HIP = 5,         /* the HIP runtime reported an error                */
     PA_ERR_NO_BLOCKS = 6,   /* block pool: not enough free blocks (nothing changed) */
     PA_ERR_BAD_ID = 7,      /* block pool: unknown or released sequence / block id */
-    PA_ERR_DEVICE_CHECK = 8 /* checked mode: a length or used table entry breaks
+    PA_ERR_DEVICE_CHECK = 8,/* checked mode: a length or used table entry breaks
                                the preconditions; no attention kernel ran       */
+    PA_ERR_SCRATCH = 9      /* pa_decode_noalloc: the plan needs more partial-
+                               result space than PA_NOALLOC_SCRATCH_BYTES        */
 } pa_status;
 
 /* Kernel families (pa_config.kernel). */
@@ -190,6 +192,32 @@ pa_status pa_decode_ex(const void *query, const void *key_cache,
                        int max_blocks, pa_dtype dtype, pa_dtype out_dtype,
                        const pa_config *cfg, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* Bytes of the static device scratch of pa_decode_noalloc (per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * pa_decode_noalloc -- pa_decode_ex for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as pa_decode_ex
+ * without the workspace: the split plan's partial results go to a static
+ * device array of PA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing.
+ *
+ * Limit: a plan whose workspace (pa_decode_plan's workspace_bytes) exceeds
+ * PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_SCRATCH before anything runs; a
+ * longer cfg->partition_tokens shrinks it (the workspace holds
+ * S * Hq * max_partitions * (D + 2) fp32 values, 256-byte aligned parts).
+ * The scratch is shared by every call on one GPU and keeps the last call's
+ * partial results: calls that overlap on one GPU (several streams or host
+ * threads) race and must be serialised by the caller.
+ */
+pa_status pa_decode_noalloc(const void *query, const void *key_cache,
+                            const void *value_cache, const int32_t *block_tables,
+                            const int32_t *seq_lens, float scale, void *out,
+                            int S, int Hq, int Hkv, int D, int B, int NB,
+                            int max_blocks, pa_dtype dtype, pa_dtype out_dtype,
+                            const pa_config *cfg, void *stream);
 
 /*
  * pa_write_kv -- store new tokens' keys and values into their cache slots

@@ -24,7 +24,9 @@ HEADER = os.path.join(INCLUDE, "pa_decode.h")
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 # pa_status
 (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP,
- PA_ERR_NO_BLOCKS, PA_ERR_BAD_ID, PA_ERR_DEVICE_CHECK) = range(9)
+ PA_ERR_NO_BLOCKS, PA_ERR_BAD_ID, PA_ERR_DEVICE_CHECK, PA_ERR_SCRATCH) = range(10)
+# bytes of the static device scratch of pa_decode_noalloc (PA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # pa_kernel
 KERNEL_AUTO, KERNEL_GENERIC, KERNEL_VALU, KERNEL_MFMA = range(4)
 KERNELS = {"auto": KERNEL_AUTO, "generic": KERNEL_GENERIC, "valu": KERNEL_VALU, "mfma": KERNEL_MFMA}
@@ -90,6 +92,8 @@ def load():
     lib.pa_prefill.restype = _INT
     lib.pa_prefill.argtypes = ([_PTR] * 6 + [ctypes.c_float, _PTR] + mq_shape +
                                [ctypes.POINTER(PaConfig), _PTR, ctypes.c_size_t, _PTR])
+    lib.pa_decode_noalloc.restype = _INT
+    lib.pa_decode_noalloc.argtypes = tensors + _SHAPE + [ctypes.POINTER(PaConfig), _PTR]
     lib.pa_check_inputs.restype = _INT
     lib.pa_check_inputs.argtypes = [_PTR, _PTR] + [_INT] * 4 + [_PTR, _PTR]
     lib.pa_get_device_error.restype = _INT
@@ -246,6 +250,35 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     _check(lib.pa_decode_ex(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
                             block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
                             out.data_ptr(), *shape, ctypes.byref(cfg), ws_ptr, ws_bytes, st))
+    return out
+
+
+def decode_noalloc(query, key_cache, value_cache, block_tables, seq_lens, scale, out, *,
+                   kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, stream=None,
+                   check: Optional[bool] = None) -> torch.Tensor:
+    """``decode`` through pa_decode_noalloc: the split plan's partial results
+    go to the library's static device scratch, and nothing is allocated here
+    either (``out`` must be given).  Calls that overlap on one GPU race for
+    the scratch."""
+    lib = load()
+    for name, t in (("query", query), ("key_cache", key_cache), ("value_cache", value_cache),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens), ("out", out)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if not (query.dtype == key_cache.dtype == value_cache.dtype):
+        raise TypeError("query, key_cache and value_cache must share one dtype")
+    if value_cache.shape != key_cache.shape or out.shape != query.shape:
+        raise ValueError("cache or output shapes do not match")
+    shape = _shape_args(query, key_cache, block_tables, out.dtype)
+    if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
+        raise ValueError("seq_lens / block_tables do not match the batch size")
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
+    _check(lib.pa_decode_noalloc(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+                                 block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                 out.data_ptr(), *shape, ctypes.byref(cfg),
+                                 _stream_handle(stream, query.device)))
     return out
 
 

@@ -490,6 +490,27 @@ pa_status pa_decode(const void *query, const void *key_cache, const void *value_
                         workspace_bytes, stream);
 }
 
+pa_status pa_decode_noalloc(const void *query, const void *key_cache, const void *value_cache,
+                            const int32_t *block_tables, const int32_t *seq_lens, float scale,
+                            void *out, int S, int Hq, int Hkv, int D, int B, int NB,
+                            int max_blocks, pa_dtype dtype, pa_dtype out_dtype,
+                            const pa_config *cfg, void *stream) {
+    pa_plan plan;
+    pa_status st = make_plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype, cfg, &plan);
+    if (st != PA_OK) return st;
+    if (plan.workspace_bytes > pa::kNoAllocScratchBytes) return PA_ERR_SCRATCH;
+    if (S == 0) return PA_OK;
+    if (!query || !key_cache || !value_cache || !block_tables || !seq_lens || !out)
+        return PA_ERR_NULL;
+    void *ws = nullptr;
+    if (plan.workspace_bytes &&
+        pa::noalloc_scratch(static_cast<hipStream_t>(stream), &ws) != hipSuccess)
+        return PA_ERR_HIP;
+    return pa_decode_ex(query, key_cache, value_cache, block_tables, seq_lens, scale, out, S, Hq,
+                        Hkv, D, B, NB, max_blocks, dtype, out_dtype, cfg, ws,
+                        ws ? pa::kNoAllocScratchBytes : 0, stream);
+}
+
 static int dtype_size(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 
 pa_status pa_write_kv(const void *key, const void *value, const int32_t *slot_mapping,
@@ -577,6 +598,9 @@ const char *pa_status_string(pa_status status) {
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the block pool has too few free blocks";
     case PA_ERR_BAD_ID: return "PA_ERR_BAD_ID: unknown or released sequence or block id";
+    case PA_ERR_SCRATCH:
+        return "PA_ERR_SCRATCH: the plan's partial results exceed the static scratch of "
+               "pa_decode_noalloc (PA_NOALLOC_SCRATCH_BYTES); use longer partitions";
     case PA_ERR_DEVICE_CHECK:
         return "PA_ERR_DEVICE_CHECK: a sequence length or used block-table entry breaks the "
                "preconditions (checked mode); nothing was launched";

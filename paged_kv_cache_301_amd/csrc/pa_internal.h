@@ -30,6 +30,11 @@ hipError_t library_check(const int32_t *block_tables, const int32_t *seq_lens,
 // Synchronise `st`, read and clear the sticky error word of its device.
 hipError_t read_device_error(hipStream_t st, int *set, int *first_bad);
 
+// pa_decode_noalloc: bytes of the static scratch (pa_noalloc.hip) and its
+// device address on the stream's device.
+constexpr size_t kNoAllocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(hipStream_t st, void **ptr);
+
 // A 1-D launch of `groups` work-groups of `threads` threads fits the
 // hardware: grid.x <= 2^31 - 1 and grid.x * threads < 2^32.
 inline bool grid_fits(long long groups, long long threads) {

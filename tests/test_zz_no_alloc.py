@@ -1,0 +1,98 @@
+"""pa_decode_noalloc (no device allocation: partial results in the library's
+static per-GPU scratch) against pa_decode_ex with a caller-owned workspace,
+through the C ABI: two calls in a row per workload, the second smaller (it
+runs on the scratch the first left behind), bit-identical outputs, both
+within the oracle's bound."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_check import check
+from paged_kv_cache_301_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _raw_noalloc(lib, w, out, cfg, stream):
+    shape = binding._shape_args(w.query, w.key_cache, w.block_tables, out.dtype)
+    return lib.pa_decode_noalloc(w.query.data_ptr(), w.key_cache.data_ptr(),
+                                 w.value_cache.data_ptr(), w.block_tables.data_ptr(),
+                                 w.seq_lens.data_ptr(), ctypes.c_float(w.scale), out.data_ptr(),
+                                 *shape, ctypes.byref(cfg), stream.cuda_stream)
+
+
+def _raw_ex(lib, w, out, cfg, ws, stream):
+    shape = binding._shape_args(w.query, w.key_cache, w.block_tables, out.dtype)
+    return lib.pa_decode_ex(w.query.data_ptr(), w.key_cache.data_ptr(), w.value_cache.data_ptr(),
+                            w.block_tables.data_ptr(), w.seq_lens.data_ptr(),
+                            ctypes.c_float(w.scale), out.data_ptr(), *shape, ctypes.byref(cfg),
+                            ws.data_ptr() if ws is not None else None,
+                            ws.numel() if ws is not None else 0, stream.cuda_stream)
+
+
+CASES = [
+    # (workload, overrides of the first call, overrides of the second, kernel, partition)
+    ("mha_7b", {}, {"S": 9, "seed": 31}, "auto", 0),
+    ("gqa_70b", {}, {"S": 20, "seed": 32}, "auto", 0),
+    ("gqa_long", {"B": 16}, {"S": 3, "seed": 33, "B": 16}, "auto", 0),
+    ("mqa", {}, {"S": 40, "seed": 34}, "auto", 0),
+    ("mha_small", {}, {"S": 3, "seed": 35}, "valu", 64),
+]
+
+
+@pytest.mark.parametrize("name,first,second,kernel,part", CASES)
+def test_noalloc_matches_workspace_entry_point(name, first, second, kernel, part):
+    print(f"case: no-allocation entry point, {name} {first} then {second}", flush=True)
+    lib = binding.load()
+    stream = torch.cuda.current_stream(DEV)
+    cfg = binding.PaConfig(binding.KERNELS[kernel], part, 0, 0, 0)
+    for over in (first, second):
+        over = dict(over)
+        seed = over.pop("seed", None)
+        if seed is not None:
+            over["seed"] = seed
+        w = workloads.make_workload(name, device=DEV, poison=True, **over)
+        p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype,
+                         torch.float32, kernel=kernel, partition_tokens=part)
+        assert p["workspace_bytes"] <= binding.NOALLOC_SCRATCH_BYTES
+        ws = (torch.empty(p["workspace_bytes"], dtype=torch.uint8, device=DEV)
+              if p["workspace_bytes"] else None)
+        a = torch.full(w.query.shape, float("nan"), dtype=torch.float32, device=DEV)
+        b = torch.full_like(a, float("nan"))
+        assert _raw_ex(lib, w, b, cfg, ws, stream) == binding.PA_OK
+        assert _raw_noalloc(lib, w, a, cfg, stream) == binding.PA_OK
+        torch.cuda.synchronize()
+        print(f"  S={w.S} plan {p}", flush=True)
+        assert torch.equal(a, b), "no-allocation result differs from the workspace entry point"
+        check(a, oracle.decode(w.query, w.key_cache, w.value_cache, w.block_tables,
+                               w.seq_lens, w.scale), w.dtype, f"noalloc {name}")
+    # the binding's wrapper, native output type
+    o = torch.empty_like(w.query)
+    binding.decode_noalloc(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                           w.scale, o, kernel=kernel, partition_tokens=part)
+    ref = binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                         w.scale, kernel=kernel, partition_tokens=part)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+
+
+def test_noalloc_rejects_plans_beyond_the_scratch():
+    """A split plan whose partial results exceed the static scratch is refused
+    before anything runs; a longer partition makes it fit."""
+    print("case: no-allocation entry point, scratch limit", flush=True)
+    lib = binding.load()
+    fake = 1 << 20     # never dereferenced: the call is refused on the host
+    args = (fake,) * 5 + (ctypes.c_float(0.1), fake)
+    S, Hq, Hkv, mb = 1024, 64, 8, 2048          # 1024 x 64 rows x 32 partitions x 130 floats
+    cfg = binding.PaConfig(binding.KERNEL_MFMA, 1024, 0, 0, 0)
+    p = binding.plan(S, Hq, Hkv, 128, 16, 100, mb, torch.bfloat16, kernel="mfma",
+                     partition_tokens=1024)
+    assert p["workspace_bytes"] > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.pa_decode_noalloc(*args, S, Hq, Hkv, 128, 16, 100, mb, binding.PA_BF16,
+                                 binding.PA_BF16, ctypes.byref(cfg), None) == binding.PA_ERR_SCRATCH
+    assert "scratch" in binding.status_string(binding.PA_ERR_SCRATCH)
