@@ -75,8 +75,9 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
     for (int kk = 0; kk < 4; ++kk) {
         uint4 w = *reinterpret_cast<const uint4 *>(qrow + 8 * g + 32 * kk);
         if (!head_ok) w = make_uint4(0, 0, 0, 0);
-        qf[kk] = bitcast<Vec>(w);
+        qf[kk] = signed_query(bitcast<Vec>(w), a.scale_log2);
     }
+    const float sc = score_scale(a.scale_log2);
 
     MfmaState<T> st;
 #pragma unroll
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();   // every wave's rows visible
             const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-            mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, a.scale_log2);
+            mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
             __syncthreads();   // reads done before the next stage overwrites LDS
         }
         st.l += shfl_xor(st.l, 16);

@@ -35,7 +35,7 @@ namespace pa {
 namespace mfma {
 
 constexpr int kD = kHeadDim;
-constexpr float kRescaleSlack = 8.f;   // see mfma_subtile
+constexpr float kRescaleSlack = 8.f;   // see mfma_tiles
 
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
@@ -53,15 +53,69 @@ template <> struct Mfma<_Float16> {
 
 // Two-term split of the probabilities for the 16-bit matrix-core operand:
 // hi = round(p), lo = round(p - hi), so hi + lo carries 2 * (mantissa + 1)
-// bits of p and the P.V product keeps fp32-level accuracy.
+// bits of p and the P.V product keeps fp32-level accuracy.  Each pair is
+// rounded once with a packed conversion (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32) and hi is read back from those bits, so no element is
+// converted twice.
+template <typename T> struct Split;
+template <> struct Split<__bf16> {
+    __device__ static void run(const float (&p)[8], bf16x8 &hi, bf16x8 &lo) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x2 hv = {(__bf16)p[2 * j], (__bf16)p[2 * j + 1]};
+            h[j] = bitcast<uint32_t>(hv);
+            // a bfloat16 widens to fp32 by appending 16 zero bits: element 0
+            // moves to the upper half (byte select), element 1 is masked
+            const float h0 = bitcast<float>(__builtin_amdgcn_perm(h[j], h[j], 0x01000c0cu));
+            const float h1 = bitcast<float>(h[j] & 0xffff0000u);
+            const bf16x2 lv = {(__bf16)(p[2 * j] - h0), (__bf16)(p[2 * j + 1] - h1)};
+            l[j] = bitcast<uint32_t>(lv);
+        }
+        hi = bitcast<bf16x8>(make_uint4(h[0], h[1], h[2], h[3]));
+        lo = bitcast<bf16x8>(make_uint4(l[0], l[1], l[2], l[3]));
+    }
+};
+template <> struct Split<_Float16> {
+    __device__ static void run(const float (&p)[8], f16x8 &hi, f16x8 &lo) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f16x2 hv = {(_Float16)p[2 * j], (_Float16)p[2 * j + 1]};
+            h[j] = bitcast<uint32_t>(hv);
+            // an identity byte select keeps the compiler from converting the
+            // two elements again one by one
+            const f16x2 hb = bitcast<f16x2>(__builtin_amdgcn_perm(h[j], h[j], 0x07060504u));
+            const f16x2 lv = {(_Float16)(p[2 * j] - (float)hb[0]),
+                              (_Float16)(p[2 * j + 1] - (float)hb[1])};
+            l[j] = bitcast<uint32_t>(lv);
+        }
+        hi = bitcast<f16x8>(make_uint4(h[0], h[1], h[2], h[3]));
+        lo = bitcast<f16x8>(make_uint4(l[0], l[1], l[2], l[3]));
+    }
+};
+
 template <typename T, typename Vec>
 __device__ __forceinline__ void split_probs(const float (&p)[8], Vec &hi, Vec &lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const T h = (T)p[j];
-        hi[j] = h;
-        lo[j] = (T)(p[j] - (float)h);
-    }
+    Split<T>::run(p, hi, lo);
+}
+
+// Scores enter the softmax as fma(acc, sc, -m) with sc = |scale * log2(e)|:
+// the query fragments carry the sign of the scale (flipping a 16-bit sign bit
+// is exact), and a zero scale becomes a zero query with sc = 1 (every score
+// exactly 0).  The raw products then order like the scores, so maxima are
+// taken on them and scaled once.
+template <typename Vec>
+__device__ __forceinline__ Vec signed_query(Vec q, float scale_log2) {
+    const uint4 u = bitcast<uint4>(q);
+    if (scale_log2 == 0.f) return bitcast<Vec>(make_uint4(0, 0, 0, 0));
+    if (scale_log2 < 0.f)
+        return bitcast<Vec>(make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u, u.z ^ 0x80008000u,
+                                       u.w ^ 0x80008000u));
+    return q;
+}
+__device__ __forceinline__ float score_scale(float scale_log2) {
+    return scale_log2 == 0.f ? 1.f : fabsf(scale_log2);
 }
 
 // LDS images of one iteration: 32 token rows of 256 bytes (16 chunks of 16
@@ -124,12 +178,12 @@ __device__ __forceinline__ void mfma_stage(const KVTile &tile, uint4 *klds, uint
 // it, so the matrix core has independent work while the vector unit waits,
 // and one maximum / rescale step serves all NS sub-tiles.  Tokens at or past
 // t_end (the partition end, wave-uniform; t0 < t_end) are masked; sub-tiles
-// that end before it need no mask.
+// that end before it need no mask.  sc: the score scale in exp2 units,
+// positive (the query fragments carry its sign, see signed_query).
 template <typename T, int NS>
 __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma<T>::Vec (&qf)[4],
                                            const uint4 (*klds)[32 * 16], const uint4 (*vlds)[32 * 16],
-                                           int t0, int nsub, int t_end, int g, int i,
-                                           float scale_log2) {
+                                           int t0, int nsub, int t_end, int g, int i, float sc) {
     using M = Mfma<T>;
     using Vec = typename M::Vec;
     // scores: A operand = chunk 4kk + g of row 16h + i (swizzle swz_k = i)
@@ -147,6 +201,7 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
             }
         }
     }
+    // raw products, masked to -inf past the partition
     float x[NS][8];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -156,21 +211,22 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
             for (int j = 0; j < 8; ++j) x[u][j] = kNegInf;
         } else if (tu + 32 <= t_end) {                // uniform: no token masked
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[u][j] = acc[u][j >> 2][j & 3] * scale_log2;
+            for (int j = 0; j < 8; ++j) x[u][j] = acc[u][j >> 2][j & 3];
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                x[u][j] = (tu + 16 * (j >> 2) + 4 * g + (j & 3) < t_end)
-                              ? acc[u][j >> 2][j & 3] * scale_log2 : kNegInf;
+                x[u][j] = (tu + 16 * (j >> 2) + 4 * g + (j & 3) < t_end) ? acc[u][j >> 2][j & 3]
+                                                                         : kNegInf;
         }
     }
-    float mt = x[0][0];
+    float mr = x[0][0];
 #pragma unroll
     for (int u = 0; u < NS; ++u)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mt = fmaxf(mt, x[u][j]);
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
+        for (int j = 0; j < 8; ++j) mr = fmaxf(mr, x[u][j]);
+    mr = fmaxf(mr, shfl_xor(mr, 16));
+    mr = fmaxf(mr, shfl_xor(mr, 32));
+    const float mt = mr * sc;                        // the column's maximum score
     // The reference point st.m moves only when a column's maximum exceeds it
     // by more than kRescaleSlack (log2 units; always on the first sub-tile,
     // where st.m = -inf): otherwise the weights are taken against the stale
@@ -189,7 +245,7 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
         st.m = mn;
     }
     // st.m is finite here: the first sub-tile (t0 < t_end) has a valid token
-    const float mref = st.m;
+    const float mneg = -st.m;
 
     const int row_a = 4 * g + (i >> 2);
     const int sw = swz_v(row_a);
@@ -201,7 +257,7 @@ __device__ __forceinline__ void mfma_tiles(MfmaState<T> &st, const typename Mfma
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(x[u][j] - mref);
+            p[j] = fast_exp2(fmaf(x[u][j], sc, mneg));
             ps += p[j];
         }
         Vec phi, plo;

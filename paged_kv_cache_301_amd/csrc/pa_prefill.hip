@@ -47,6 +47,8 @@ static_assert(16 * kGroups * kWaves == kPrefillColumns, "columns per work-group"
 constexpr int kLoads = kTileLoads / kWaves;         // load instructions per operand per wave
 constexpr int kXcds = 8;   // accelerator dies: consecutive work-group ids alternate between them
 
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 // This wave's quarter of a sub-tile (rows 4 (k0 + k) + g, chunk i) to the
 // swizzled LDS images.
 __device__ __forceinline__ void stage_quarter(const KVTileN<kLoads> &tile, uint4 *klds, uint4 *vlds,
@@ -59,15 +61,16 @@ __device__ __forceinline__ void stage_quarter(const KVTileN<kLoads> &tile, uint4
     }
 }
 
-// One staged 32-token sub-tile starting at t0 for the wave's column
-// groups.  lim[j]: tokens column group j's lane may see; t_full: uniform
-// bound below which no column masks.
-template <typename T>
+// One staged 32-token sub-tile starting at t0 for the wave's column groups.
+// MASK: some column may not see every token of the sub-tile (lim[j]: tokens
+// column group j's lane may see); without it no score is masked, which is
+// every sub-tile below the block's first query position.  sc: the score
+// scale in exp2 units, positive (see signed_query).
+template <typename T, bool MASK>
 __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
                                                const typename Mfma<T>::Vec (&qf)[kGroups][4],
                                                const uint4 *klds, const uint4 *vlds, int t0,
-                                               const int (&lim)[kGroups], int t_full, int g, int i,
-                                               float scale_log2) {
+                                               const int (&lim)[kGroups], int g, int i, float sc) {
     using M = Mfma<T>;
     using Vec = typename M::Vec;
     // K fragments: A operand = chunk 4kk + g of row 16h + i (swizzle swz_k = i)
@@ -97,36 +100,51 @@ __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
         struct { i16x4 a, b; } raw = {lds_read_tr16(vlds, off), lds_read_tr16(vlds, off + 16 * kRowBytes)};
         vf[n] = bitcast<Vec>(raw);
     }
-    const bool full = t0 + 32 <= t_full;          // uniform
+    // raw products (masked to -inf) and each column's maximum, scaled once
+    float x[kGroups][8];
+    float mt[kGroups];
+    bool grow[kGroups];
+    bool grow_any = false;
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
-        float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float v = acc[j][e >> 2][e & 3] * scale_log2;
-            x[e] = (full || t0 + 16 * (e >> 2) + 4 * g + (e & 3) < lim[j]) ? v : kNegInf;
+            const float v = acc[j][e >> 2][e & 3];
+            x[j][e] = (!MASK || t0 + 16 * (e >> 2) + 4 * g + (e & 3) < lim[j]) ? v : kNegInf;
         }
-        float mt = x[0];
+        float m = x[j][0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
-        // deferred rescale, as in mfma_tiles
-        const bool grow = mt > st[j].m + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float mn = grow ? mt : st[j].m;
-            const float alpha = grow ? fast_exp2(st[j].m - mn) : 1.f;
+        for (int e = 1; e < 8; ++e) m = fmaxf(m, x[j][e]);
+        m = fmaxf(m, shfl_xor(m, 16));
+        m = fmaxf(m, shfl_xor(m, 32));
+        mt[j] = m * sc;
+        grow[j] = mt[j] > st[j].m + kRescaleSlack;    // false while mt = -inf
+        grow_any = grow_any || grow[j];
+    }
+    // deferred rescale, as in mfma_tiles: one wave-uniform branch for all the
+    // wave's groups, so the straight-line code below lets the matrix core
+    // work through one group's P.V while the vector unit computes the next
+    // group's probabilities
+    if (__builtin_amdgcn_ballot_w64(grow_any) != 0) {
+#pragma unroll
+        for (int j = 0; j < kGroups; ++j) {
+            const float mn = grow[j] ? mt[j] : st[j].m;
+            const float alpha = grow[j] ? fast_exp2(st[j].m - mn) : 1.f;
             st[j].l *= alpha;
 #pragma unroll
             for (int n = 0; n < 8; ++n) st[j].o[n] *= alpha;
             st[j].m = mn;
         }
-        const float mref = st[j].m == kNegInf ? 0.f : st[j].m;
+    }
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+        // a column that has seen no token yet keeps zero weights
+        const float mneg = st[j].m == kNegInf ? 0.f : -st[j].m;
         float p[8];
         float ps = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = fast_exp2(x[e] - mref);
+            p[e] = fast_exp2(fmaf(x[j][e], sc, mneg));
             ps += p[e];
         }
         st[j].l += ps;
@@ -182,6 +200,7 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
     int lim[kGroups], lim_eff[kGroups], rows[kGroups], heads[kGroups];
     bool ok[kGroups];
     Vec qf[kGroups][4];
+    const float sc = score_scale(a.scale_log2);
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
         const int c = 16 * kGroups * w + 16 * j + i;
@@ -197,7 +216,7 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
         for (int kk = 0; kk < 4; ++kk) {
             uint4 v = *reinterpret_cast<const uint4 *>(qrow + 8 * g + 32 * kk);
             if (!ok[j]) v = make_uint4(0, 0, 0, 0);
-            qf[j][kk] = bitcast<Vec>(v);
+            qf[j][kk] = signed_query(bitcast<Vec>(v), a.scale_log2);
         }
     }
 
@@ -233,28 +252,37 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
 
     // One barrier per sub-tile: a wave writes LDS image b only after the
     // barrier of the previous sub-tile, which every wave reaches after it
-    // has finished reading image b (two sub-tiles earlier).
+    // has finished reading image b (two sub-tiles earlier).  Sub-tiles come
+    // in pairs (images 0 and 1, register tiles ra and rb); the leading pairs
+    // that lie wholly below t_full run without the causal mask, in a loop of
+    // their own (one loop holding both forms needs more registers than two
+    // waves per SIMD allow).
     const int niter = (t_end - t_begin + 31) >> 5;
+    const int n_full = t_full > t_begin ? (t_full - t_begin) >> 5 : 0;
     const int k0 = kLoads * w;
     KVTileN<kLoads> ra, rb;
     ctx.load(ra, t_begin, k0);
-    for (int it = 0; it < niter; it += 2) {
+    auto sub_pair = [&](int it, auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
         const int t0 = t_begin + 32 * it;
         ctx.load(rb, t0 + 32, k0);
         __builtin_amdgcn_sched_barrier(0);
         stage_quarter(ra, klds[0], vlds[0], k0, g, i);
         __syncthreads();
-        subtile_groups<T>(st, qf, klds[0], vlds[0], t0, lim_eff, t_full, g, i, a.scale_log2);
+        subtile_groups<T, MASK>(st, qf, klds[0], vlds[0], t0, lim_eff, g, i, sc);
         __builtin_amdgcn_sched_barrier(0);
         ctx.load(ra, t0 + 64, k0);
         __builtin_amdgcn_sched_barrier(0);
         if (it + 1 < niter) {
             stage_quarter(rb, klds[1], vlds[1], k0, g, i);
             __syncthreads();
-            subtile_groups<T>(st, qf, klds[1], vlds[1], t0 + 32, lim_eff, t_full, g, i, a.scale_log2);
+            subtile_groups<T, MASK>(st, qf, klds[1], vlds[1], t0 + 32, lim_eff, g, i, sc);
         }
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    int it = 0;
+    for (; it + 2 <= n_full; it += 2) sub_pair(it, BoolTag<false>{});
+    for (; it < niter; it += 2) sub_pair(it, BoolTag<true>{});
 
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
