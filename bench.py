@@ -79,7 +79,8 @@ def parse():
                     help="decode: also time the step captured in one HIP graph and replayed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-peak", action="store_true",
-                    help="decode: skip the plain 4 GiB device read used as the measured HBM peak")
+                    help="decode: skip the plain device reads (the 4 GiB measured HBM peak and "
+                         "each configuration's same-size read floor)")
     ap.add_argument("--no-extra-configs", action="store_true",
                     help="decode: skip the other decode configurations (C2 mha_small, C4 "
                          "gqa_70b, C5 gqa_long at B = 16) measured after the headline")
@@ -268,13 +269,37 @@ def measure_decode(w, args, dev, scratch, kernel="auto", partition_tokens=0, kv_
     return plan, t, (step, args_, kw)
 
 
-def decode_summary(w, plan, t, kname):
+def plain_read_floor(nbytes, args, dev, scratch):
+    """Cold median of the library's plain streaming read (pa_read_bytes) over
+    a contiguous buffer of the same size as a workload's unique K/V: what one
+    launch moving that many bytes takes on this GPU, the floor for a step."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_301_amd import binding
+    nbytes = (nbytes + 15) // 16 * 16
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    binding.read_bytes(buf, sink, stream=stream)
+    ms = evict_and_time(lambda: binding.read_bytes(buf, sink, stream=stream), args.steps, stream,
+                        scratch)
+    del buf
+    med = float(np.median(ms))
+    return {"median_us": round(med * 1e3, 2), "gbs": round(nbytes / (med * 1e-3) / 1e9, 2),
+            "bytes": nbytes}
+
+
+def decode_summary(w, plan, t, kname, floor=None):
     """Rates of one measured decode workload: logical and unique bytes."""
     kv = w.kv_bytes()
     unique = w.unique_kv_bytes() if w.spec.prefix_tokens else kv
     step_s = t["cold"]["median_us"] * 1e-6
     k_s = t["partitions"]["mean_us"] * 1e-6
-    return {
+    extra = {}
+    if floor:
+        extra = {"plain_read_floor": floor,
+                 "step_vs_floor": round(floor["median_us"] / t["cold"]["median_us"], 4)}
+    return {**extra,
         "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "B": w.B,
         "tokens": int(w.lens.sum()), "kv_bytes": kv, "unique_kv_bytes": unique,
         "kernel": kname, "partition_tokens": plan["partition_tokens"], "split": bool(plan["split"]),
@@ -613,7 +638,9 @@ def main():
                                                 partition_tokens=args.partition_tokens,
                                                 kv_reuse=kv_reuse)
     kname = KERNEL_NAMES[plan["kernel"]]
-    summ = decode_summary(w, plan, t, kname)
+    uniq0 = w.unique_kv_bytes() if w.spec.prefix_tokens else w.kv_bytes()
+    floor = None if args.no_read_peak else plain_read_floor(uniq0, args, dev, scratch)
+    summ = decode_summary(w, plan, t, kname, floor)
     kv = w.kv_bytes()
     step_ms = t["cold"]["median_us"] * 1e-3
     gbs = kv / (step_ms * 1e-3) / 1e9
@@ -658,11 +685,14 @@ def main():
             wx = workloads.make_workload(name, device=dev, poison=False, **over)
             torch.cuda.synchronize()
             px, tx, _ = measure_decode(wx, args, dev, scratch, kv_reuse=kv_reuse)
-            extra[key] = decode_summary(wx, px, tx, KERNEL_NAMES[px["kernel"]])
+            ux = wx.unique_kv_bytes() if wx.spec.prefix_tokens else wx.kv_bytes()
+            fx = None if args.no_read_peak else plain_read_floor(ux, args, dev, scratch)
+            extra[key] = decode_summary(wx, px, tx, KERNEL_NAMES[px["kernel"]], fx)
             e = extra[key]
             print(f"[bench] {key}: cold step {e['step_cold_us']['median_us']:.1f} us "
                   f"({e['gbs']:.0f} GB/s logical, {e['unique_hbm_frac'] * 100:.1f} % of 8 TB/s "
-                  f"on unique bytes), kernel {e['kernel_cold_us']['mean_us']:.1f} us",
+                  f"on unique bytes), kernel {e['kernel_cold_us']['mean_us']:.1f} us, plain read "
+                  f"of the same bytes {(e.get('plain_read_floor') or {}).get('median_us', 0):.1f} us",
                   file=sys.stderr, flush=True)
             del wx
     del scratch
@@ -699,6 +729,8 @@ def main():
         "unique_hbm_frac": round(unique / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                            if unique else None,
         "step_cold_us": t["cold"],
+        "plain_read_floor": summ.get("plain_read_floor"),
+        "step_vs_floor": summ.get("step_vs_floor"),
         "kernel_us": {"partitions": t["partitions"], "combine": t["combine"]},
         "warm": {**t["warm"], "value": round(kv / (t["warm"]["ms_per_step"] * 1e-3) / 1e9, 2)},
         "graph": graph,

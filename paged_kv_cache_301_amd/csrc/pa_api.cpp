@@ -98,7 +98,7 @@ bool supports_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
 // kernels stage the table when B % 4 != 0).
 long long table_cap(int kernel, int B) {
     const bool staged = (kernel == PA_KERNEL_VALU || kernel == PA_KERNEL_MFMA) && B % 4 != 0;
-    return staged ? 1024LL * B : (long long)INT_MAX;
+    return staged ? (long long)pa::kTableLds * B : (long long)INT_MAX;
 }
 
 // Threads per work-group of a decode kernel family (the matrix-core kernel
@@ -264,7 +264,7 @@ pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB,
         if (part >= max_ctx) part = ((max_ctx > 0 ? max_ctx : 1) + 31) / 32 * 32;
         const long long min_part = (max_ctx + pa::kMaxPartitions - 1) / pa::kMaxPartitions;
         if (part < min_part) part = (min_part + 31) / 32 * 32;
-        const long long cap = B % 4 != 0 ? 1024LL * B : (long long)INT_MAX;
+        const long long cap = B % 4 != 0 ? (long long)pa::kTableLds * B : (long long)INT_MAX;
         if (part > cap) part = cap / 32 * 32;
         if (part > INT_MAX) part = INT_MAX / 32 * 32;
         const long long parts = max_ctx > 0 ? (max_ctx + part - 1) / part : 1;

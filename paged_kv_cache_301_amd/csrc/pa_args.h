@@ -40,6 +40,11 @@ constexpr int kTileTokens = 32;
 // Partitions per (sequence, head): the partition index is grid dimension y.
 constexpr int kMaxPartitions = 65535;
 
+// Entries of a partition's block-table slice the tiled kernels copy to LDS
+// (blocks of fewer than 4 tokens); the host caps such partitions at
+// kTableLds * B tokens.
+constexpr int kTableLds = 1024;
+
 // Largest batch whose lengths one wave holds in registers for the live-item
 // decode of the tiled decode kernels (pa_sched.h); larger batches use the
 // rectangular grid.

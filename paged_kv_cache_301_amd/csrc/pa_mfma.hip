@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
         ctx.tv.j0 = t_begin >> a.log2B;
         ctx.tbl = tbl;
         if constexpr (!SCALAR) {
-            stage_table(tbl, ctx.tv, t_begin, t_end, threadIdx.x, 64 * W);
+            stage_table<64 * W>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
             __syncthreads();
         }
 
@@ -113,17 +113,39 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
         // instead of 184 and was 1-4 % slower.)  The scheduling barriers keep
         // the compiler from sinking that prefetch below the products.
         KVTile tile;
-        ctx.load(tile, tw);
-        for (int it = 0; it < niter; ++it) {
-            const int t0 = t_begin + kIter * it;
-            mfma_stage(tile, klds[w], vlds[w], g, i);
-            __builtin_amdgcn_sched_barrier(0);
-            if (it + 1 < niter) ctx.load(tile, tw + kIter * (it + 1));   // uniform
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();   // every wave's rows visible
-            const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-            mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
-            __syncthreads();   // reads done before the next stage overwrites LDS
+        if constexpr (SCALAR) {
+            ctx.load(tile, tw);
+            for (int it = 0; it < niter; ++it) {
+                const int t0 = t_begin + kIter * it;
+                mfma_stage(tile, klds[w], vlds[w], g, i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (it + 1 < niter) ctx.load(tile, tw + kIter * (it + 1));   // uniform
+                __builtin_amdgcn_sched_barrier(0);
+                __syncthreads();   // every wave's rows visible
+                const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
+                mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
+                __syncthreads();   // reads done before the next stage overwrites LDS
+            }
+        } else {
+            // table in LDS (blocks of fewer than 4 tokens, one per row): the
+            // next-but-one sub-tile's block ids are looked up while this one
+            // is computed
+            int ids[kTileLoads];
+            ctx.ids(ids, tw);
+            ctx.load_ids(tile, ids, tw);
+            ctx.ids(ids, tw + kIter);
+            for (int it = 0; it < niter; ++it) {
+                const int t0 = t_begin + kIter * it;
+                mfma_stage(tile, klds[w], vlds[w], g, i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (it + 1 < niter) ctx.load_ids(tile, ids, tw + kIter * (it + 1));   // uniform
+                __builtin_amdgcn_sched_barrier(0);
+                ctx.ids(ids, tw + kIter * (it + 2));
+                __syncthreads();   // every wave's rows visible
+                const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
+                mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
+                __syncthreads();   // reads done before the next stage overwrites LDS
+            }
         }
         st.l += shfl_xor(st.l, 16);
         st.l += shfl_xor(st.l, 32);

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
     ctx.tv.j0 = t_begin >> a.log2B;
     ctx.tbl = tbl;
     if constexpr (!SCALAR) {
-        stage_table(tbl, ctx.tv, t_begin, t_end, threadIdx.x, 64 * kWaves);
+        stage_table<64 * kWaves>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
         __syncthreads();
     }
 

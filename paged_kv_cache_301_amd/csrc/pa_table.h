@@ -16,12 +16,11 @@
 //    reads its own entry from there -- again off the vmcnt queue.
 #pragma once
 
+#include "pa_args.h"
 #include "pa_device.h"
 
 namespace pa {
 
-// Entries a partition's table slice may hold in LDS.
-constexpr int kTableLds = 1024;
 
 struct TableView {
     const int32_t *row;   // block_tables[s]
@@ -29,11 +28,28 @@ struct TableView {
     int j0;               // first logical block of the partition (LDS mode)
 };
 
-// Copy the logical blocks covering tokens [t_begin, t_end) into LDS.
+// Copy the logical blocks covering tokens [t_begin, t_end) into LDS (at most
+// kTableLds entries, which the host's partition cap guarantees).  NLANES
+// threads share the copy; each issues all of its loads before its first LDS
+// write, so the copy costs one memory round trip, not one per entry it
+// handles (a one-token-block partition of 1024 tokens is 16 entries per lane
+// of a one-wave work-group).
+template <int NLANES>
 __device__ __forceinline__ void stage_table(int32_t *tbl, const TableView &tv,
-                                            int t_begin, int t_end, int lane, int nlanes) {
+                                            int t_begin, int t_end, int lane) {
+    constexpr int kPer = (kTableLds + NLANES - 1) / NLANES;
     const int nj = ((t_end - 1) >> tv.lb) - tv.j0 + 1;
-    for (int i = lane; i < nj; i += nlanes) tbl[i] = tv.row[tv.j0 + i];
+    int v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int idx = lane + u * NLANES;
+        v[u] = idx < nj ? tv.row[tv.j0 + idx] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int idx = lane + u * NLANES;
+        if (idx < nj) tbl[idx] = v[u];
+    }
 }
 
 // Physical block of token t (t must be < the sequence length).

@@ -53,6 +53,27 @@ struct TileLoader {
             tile.v[k] = load_kv16<STREAM>(vbase + off);
         }
     }
+
+    // The two halves of load(), for the LDS table path: the physical blocks
+    // of a tile's rows, looked up (LDS reads) an iteration before the loads
+    // that use them, so those loads need not wait for the lookups.
+    template <int N>
+    __device__ __forceinline__ void ids(int (&phys)[N], int t0, int k0 = 0) const {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            phys[k] = phys_block<SCALAR>(tv, tbl, min(t0 + 4 * (k0 + k) + g, t_end - 1));
+    }
+    template <int N>
+    __device__ __forceinline__ void load_ids(KVTileN<N> &tile, const int (&phys)[N], int t0,
+                                             int k0 = 0) const {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const int t = min(t0 + 4 * (k0 + k) + g, t_end - 1);
+            const size_t off = (size_t)phys[k] * block_bytes + (size_t)(t & bmask) * kRowBytes;
+            tile.k[k] = load_kv16<STREAM>(kbase + off);
+            tile.v[k] = load_kv16<STREAM>(vbase + off);
+        }
+    }
 };
 
 }  // namespace pa

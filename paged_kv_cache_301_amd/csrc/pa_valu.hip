@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         ctx.tv.j0 = t_begin >> a.log2B;
         ctx.tbl = tbl;
         if constexpr (!SCALAR) {
-            stage_table(tbl, ctx.tv, t_begin, t_end, lane, 64);
+            stage_table<64>(tbl, ctx.tv, t_begin, t_end, lane);
             __syncthreads();
         }
 
