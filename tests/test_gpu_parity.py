@@ -481,3 +481,41 @@ def test_small_config_every_row(dt):
     check(out, ref, DT[dt], f"mha_small/{dt}")
     if dt != "f32":
         check(run(w), ref, DT[dt], f"mha_small/{dt}/native")
+
+
+# ------------------------------------------- pools beyond 4 GiB, small blocks
+
+@pytest.mark.parametrize("kernel,Hq,Hkv,B", [("mfma", 16, 2, 1), ("mfma", 64, 8, 2),
+                                             ("valu", 8, 8, 1)])
+def test_pool_beyond_4gib_small_blocks(kernel, Hq, Hkv, B):
+    """Row addresses past 4 GiB: a small workload's blocks are moved to ids
+    near the top of a pool of more than 4 GiB per cache (and just below
+    4 GiB), where block id times block size overflows 32 bits.  Small blocks
+    take the most distinct ids for a given size.  The output must be
+    bit-identical to the small pool's, which is compared with the oracle on
+    every row."""
+    say(f"case: pool > 4 GiB {kernel} Hq={Hq} Hkv={Hkv} B={B}")
+    spec = workloads.WorkloadSpec("big", S=4, Hq=Hq, Hkv=Hkv, D=128, B=B, dtype="bf16",
+                                  lens=("fixed", (5, 100, 513, 900)), max_len=900,
+                                  pool=("free", 0.3), seed=61)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    kw = dict(out_dtype=torch.float32, kernel=kernel, partition_tokens=64)
+    a = run(w, **kw)
+    check(a, oracle_full(w), torch.bfloat16, f"small pool {kernel} B={B}")
+    block_bytes = Hkv * B * 128 * 2
+    NB = (1 << 32) // block_bytes + 4096
+    assert w.NB < 4096      # the two id ranges below do not meet
+    assert NB * block_bytes > (1 << 32) and NB < (1 << 24)
+    # half the blocks at the very top of the pool, half just below 4 GiB
+    pi = torch.as_tensor(np.random.default_rng(62).permutation(w.NB), device=DEV)
+    top = torch.where(pi % 2 == 0, NB - 1 - pi, (1 << 32) // block_bytes - 1 - pi)
+    big_k = torch.empty((NB, Hkv, B, 128), dtype=torch.bfloat16, device=DEV)
+    big_v = torch.empty_like(big_k)
+    big_k[top] = w.key_cache
+    big_v[top] = w.value_cache
+    bt = top[w.block_tables.long()].to(torch.int32)
+    b = binding.decode(w.query, big_k, big_v, bt, w.seq_lens, w.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), "moving blocks beyond 4 GiB changed the output"
+    del big_k, big_v
+    torch.cuda.empty_cache()
