@@ -215,6 +215,14 @@ bool supports_prefill_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
 // holds fewer than one round of four-wave groups (two per CU).
 constexpr long long kPrefillMinGroups = 512;
 
+// Columns per work-group of the multi-token kernel: 64 (two waves) when
+// every sequence's rows fit them, so a 128-column block would be at least
+// half empty for every sequence; else 128.
+int prefill_columns(int G, int max_query_len) {
+    return (long long)G * max_query_len <= pa::kPrefillColumnsNarrow ? pa::kPrefillColumnsNarrow
+                                                                     : pa::kPrefillColumns;
+}
+
 pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB, int max_blocks,
                             int max_query_len, pa_dtype dtype, pa_dtype out_dtype,
                             const pa_config *cfg, pa_plan *plan, int *q_blocks) {
@@ -243,20 +251,23 @@ pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB,
     pa_plan p{};
     *q_blocks = 0;
     if (kernel == PA_KERNEL_MFMA) {
-        const int qpb = pa::kPrefillColumns / (Hq / Hkv);
+        const int cols = prefill_columns(Hq / Hkv, max_query_len);
+        const int qpb = cols / (Hq / Hkv);
         const long long qb = (max_query_len + qpb - 1) / qpb;
         const long long groups = qb * S * Hkv;
         // grid x: the (sequence, kv head) pairs padded to whole XCD rounds,
-        // times the query blocks, of kPrefillThreads threads each
+        // times the query blocks, of 64 threads per 32 columns
         const long long grid_x = ((long long)S * Hkv + 7) / 8 * 8 * qb;
-        if (!pa::grid_fits(grid_x, pa::kPrefillThreads)) return PA_ERR_SHAPE;
+        if (!pa::grid_fits(grid_x, 2 * cols)) return PA_ERR_SHAPE;
+        // one round of resident work-groups: kPrefillMinGroups four-wave ones
+        const long long min_groups = kPrefillMinGroups * pa::kPrefillColumns / cols;
         long long part;
         if (req > 0) {
             part = req;
-        } else if (groups >= kPrefillMinGroups || max_ctx <= 256) {
+        } else if (groups >= min_groups || max_ctx <= 256) {
             part = max_ctx;                                        // one pass
         } else {
-            const long long want = (kPrefillMinGroups + groups - 1) / (groups > 0 ? groups : 1);
+            const long long want = (min_groups + groups - 1) / (groups > 0 ? groups : 1);
             part = (max_ctx + want - 1) / want;
             part = (part + 127) / 128 * 128;
             if (part < 256) part = 256;
@@ -460,6 +471,7 @@ pa_status pa_prefill(const void *query, const void *key_cache, const void *value
     a.query_start = query_start;
     a.T = T;
     a.q_blocks = qb;
+    a.prefill_columns = prefill_columns(Hq / Hkv, max_query_len);
     if (plan.split) {
         const size_t rows = (size_t)T * Hq * plan.max_partitions;
         char *ws = static_cast<char *>(workspace);

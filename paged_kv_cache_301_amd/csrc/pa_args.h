@@ -31,6 +31,7 @@ struct Args {
     const int32_t *query_start;   // [S+1] rows query_start[s] .. query_start[s+1]-1 are sequence s's
     int T;                        // query rows; query / out are [T][Hq][D]
     int q_blocks;                 // query blocks per sequence in the grid
+    int prefill_columns;          // (query token, head) columns per work-group
 };
 
 // Tokens one loop iteration of the tiled kernels covers; partitions are
@@ -51,9 +52,10 @@ constexpr int kTableLds = 1024;
 constexpr int kSchedMaxSeqs = 1024;
 
 // (query token, head) columns per work-group of the multi-token matrix-core
-// kernel: four waves of two 16-column groups.
+// kernel: four waves of two 16-column groups, or two waves when every
+// sequence's rows fit 64 columns (G * max_query_len <= 64).
 constexpr int kPrefillColumns = 128;
-constexpr int kPrefillThreads = 256;
+constexpr int kPrefillColumnsNarrow = 64;
 
 // Threads per work-group of the K / V write and block-copy kernels, and
 // bytes of one block one copy work-group moves.

@@ -13,9 +13,14 @@
 // query tokens, context partition).  Its 128 columns are (query token, head)
 // pairs, column c = token c / G, head c % G of the kv head's group, so a block
 // holds 128 / G query tokens; wave w owns columns 32 w .. 32 w + 31 as two
-// groups of 16 (the matrix core's column width).  An iteration covers one
-// 32-token sub-tile of whole K / V rows (pa_tile.h): each wave loads a quarter
-// of its rows, the four quarters meet in a double-buffered LDS image (one
+// groups of 16 (the matrix core's column width).  When every sequence's rows
+// fit 64 columns (G times the longest query chunk at most 64: a few new
+// tokens, or one token of a wide group) the work-group has two waves and 64
+// columns instead, so no block is more than half empty by construction
+// (measured: 4 new tokens on the 16-sequence batch 104 -> 70 us, on the
+// 128-sequence 8-head-group batch 366 -> 334 us).  An iteration covers one
+// 32-token sub-tile of whole K / V rows (pa_tile.h): each wave loads its
+// share of the rows, the shares meet in a double-buffered LDS image (one
 // barrier per iteration), and every wave reads the K and V^T fragments of the
 // sub-tile once and runs the two products for both of its column groups
 // with them -- twice the matrix-core work per LDS byte and per fragment read
@@ -41,20 +46,18 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 4;
-constexpr int kGroups = kPrefillColumns / (16 * kWaves);   // 16-column groups per wave
-static_assert(16 * kGroups * kWaves == kPrefillColumns, "columns per work-group");
-constexpr int kLoads = kTileLoads / kWaves;         // load instructions per operand per wave
-constexpr int kXcds = 8;   // accelerator dies: consecutive work-group ids alternate between them
+constexpr int kGroups = 2;   // 16-column groups per wave
+constexpr int kXcds = 8;     // accelerator dies: consecutive work-group ids alternate between them
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
-// This wave's quarter of a sub-tile (rows 4 (k0 + k) + g, chunk i) to the
-// swizzled LDS images.
-__device__ __forceinline__ void stage_quarter(const KVTileN<kLoads> &tile, uint4 *klds, uint4 *vlds,
-                                              int k0, int g, int i) {
+// This wave's share of a sub-tile (rows 4 (k0 + k) + g, chunk i, k < NL) to
+// the swizzled LDS images.
+template <int NL>
+__device__ __forceinline__ void stage_part(const KVTileN<NL> &tile, uint4 *klds, uint4 *vlds,
+                                           int k0, int g, int i) {
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
+    for (int k = 0; k < NL; ++k) {
         const int row = 4 * (k0 + k) + g;
         klds[row * 16 + (i ^ swz_k(row))] = tile.k[k];
         vlds[row * 16 + (i ^ swz_v(row))] = tile.v[k];
@@ -158,11 +161,15 @@ __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
     }
 }
 
-template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
-__global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kernel(Args a) {
+// NW waves per work-group (4, or 2 when every sequence's rows fit 64
+// columns): 32 NW columns.
+template <typename T, typename OutT, int G, int NW, bool SCALAR, bool STREAM>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
-    constexpr int QPB = kPrefillColumns / G;     // query tokens per work-group
-    static_assert(QPB * G == kPrefillColumns, "G divides the column count");
+    constexpr int kColumns = 16 * kGroups * NW;
+    constexpr int kLoads = kTileLoads / NW;      // load instructions per operand per wave
+    constexpr int QPB = kColumns / G;            // query tokens per work-group
+    static_assert(QPB * G == kColumns, "G divides the column count");
 
     // x: work-groups are dealt round-robin to the 8 XCDs (x mod 8); the
     // query blocks of one (sequence, kv head) pair get consecutive slots of
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
     ctx.tv.j0 = t_begin >> a.log2B;
     ctx.tbl = tbl;
     if constexpr (!SCALAR) {
-        stage_table<64 * kWaves>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
+        stage_table<64 * NW>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
         __syncthreads();
     }
 
@@ -267,14 +274,14 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
         const int t0 = t_begin + 32 * it;
         ctx.load(rb, t0 + 32, k0);
         __builtin_amdgcn_sched_barrier(0);
-        stage_quarter(ra, klds[0], vlds[0], k0, g, i);
+        stage_part(ra, klds[0], vlds[0], k0, g, i);
         __syncthreads();
         subtile_groups<T, MASK>(st, qf, klds[0], vlds[0], t0, lim_eff, g, i, sc);
         __builtin_amdgcn_sched_barrier(0);
         ctx.load(ra, t0 + 64, k0);
         __builtin_amdgcn_sched_barrier(0);
         if (it + 1 < niter) {
-            stage_quarter(rb, klds[1], vlds[1], k0, g, i);
+            stage_part(rb, klds[1], vlds[1], k0, g, i);
             __syncthreads();
             subtile_groups<T, MASK>(st, qf, klds[1], vlds[1], t0 + 32, lim_eff, g, i, sc);
         }
@@ -315,19 +322,25 @@ __global__ __launch_bounds__(64 * kWaves, kGroups > 2 ? 1 : 2) void prefill_kern
     }
 }
 
-template <typename T, typename OutT, int G>
-hipError_t launch_g(const Args &a, hipStream_t st) {
+template <typename T, typename OutT, int G, int NW>
+void launch_gw(const Args &a, hipStream_t st) {
     const long long pairs = (long long)a.S * a.Hkv;
     const dim3 grid((unsigned)((pairs + kXcds - 1) / kXcds * kXcds * a.q_blocks), a.max_parts);
-    const dim3 block(64 * kWaves);
+    const dim3 block(64 * NW);
     const bool scalar = a.B % 4 == 0;
     if (a.stream_kv) {
-        if (scalar) hipLaunchKernelGGL((prefill_kernel<T, OutT, G, true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((prefill_kernel<T, OutT, G, false, true>), grid, block, 0, st, a);
+        if (scalar) hipLaunchKernelGGL((prefill_kernel<T, OutT, G, NW, true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((prefill_kernel<T, OutT, G, NW, false, true>), grid, block, 0, st, a);
     } else {
-        if (scalar) hipLaunchKernelGGL((prefill_kernel<T, OutT, G, true, false>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((prefill_kernel<T, OutT, G, false, false>), grid, block, 0, st, a);
+        if (scalar) hipLaunchKernelGGL((prefill_kernel<T, OutT, G, NW, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((prefill_kernel<T, OutT, G, NW, false, false>), grid, block, 0, st, a);
     }
+}
+
+template <typename T, typename OutT, int G>
+hipError_t launch_g(const Args &a, hipStream_t st) {
+    if (a.prefill_columns == kPrefillColumnsNarrow) launch_gw<T, OutT, G, 2>(a, st);
+    else launch_gw<T, OutT, G, 4>(a, st);
     return hipGetLastError();
 }
 

@@ -224,15 +224,47 @@ def test_prefill_matches_oracle(kernel, dt, Hq, Hkv, B, part, out_f32):
     check(out, _oracle_full(pw), tdt, f"prefill/{kernel}/{dt}/G{Hq // Hkv}/B{B}")
 
 
+# A few new tokens per sequence (G * max_query_len <= 64): two-wave,
+# 64-column work-groups
+FEW = [
+    # (dtype, Hq, Hkv, B, partition, new tokens per sequence)
+    ("bf16", 32, 8, 16, 0, (1, 4, 16, 2, 0, 16)),
+    ("f16", 8, 8, 1, 0, (1, 30, 64, 2, 0, 64)),
+    ("bf16", 64, 1, 16, 0, (1, 1, 1, 1, 0, 1)),
+    ("bf16", 16, 1, 2, 96, (1, 4, 3, 4, 0, 2)),
+    ("bf16", 64, 2, 8, 64, (1, 2, 2, 1, 0, 2)),
+    ("f16", 16, 8, 32, 0, (1, 30, 32, 17, 0, 32)),
+]
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("Hq,Hkv,part", [(8, 8, 0), (32, 4, 64), (64, 1, 0)])
-def test_prefill_needle_positions_exact(Hq, Hkv, part):
+@pytest.mark.parametrize("out_f32", [False, True])
+@pytest.mark.parametrize("dt,Hq,Hkv,B,part,new", FEW)
+def test_prefill_few_tokens_matches_oracle(dt, Hq, Hkv, B, part, new, out_f32):
+    from gpu_check import check
+    assert (Hq // Hkv) * max(new) <= 64
+    print(f"case: prefill few tokens {dt} Hq={Hq} Hkv={Hkv} B={B} part={part} new={new} "
+          f"out_f32={out_f32}", flush=True)
+    pw = _small(dt, Hq, Hkv, B, LENS, new, seed=600 + Hq + B)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    out = b.prefill_workload(pw, out_dtype=torch.float32 if out_f32 else tdt,
+                             partition_tokens=part)
+    torch.cuda.synchronize()
+    check(out, _oracle_full(pw), tdt, f"prefill few/{dt}/G{Hq // Hkv}/B{B}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("Hq,Hkv,part,new", [(8, 8, 0, (40, 100, 64)), (32, 4, 64, (40, 100, 64)),
+                                             (64, 1, 0, (40, 100, 64)),
+                                             (32, 8, 0, (8, 16, 4)), (64, 1, 0, (1, 1, 1)),
+                                             (8, 8, 64, (40, 64, 33))])
+def test_prefill_needle_positions_exact(Hq, Hkv, part, new):
     """q = e_0, K[0] = 2048 at one token per sequence: every row at or after
     that position outputs exactly its V (which encodes block, slot and kv
     head); rows before it never see it."""
-    print(f"case: prefill needle Hq={Hq} Hkv={Hkv} part={part}", flush=True)
+    print(f"case: prefill needle Hq={Hq} Hkv={Hkv} part={part} new={new}", flush=True)
     B = 16
-    lens, new = [40, 300, 129], [40, 100, 64]
+    lens, new = [40, 300, 129], list(new)
     pw = _small("bf16", Hq, Hkv, B, lens, new, seed=77)
     w = pw.base
     kc = torch.zeros_like(w.key_cache)
