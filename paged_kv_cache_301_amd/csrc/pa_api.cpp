@@ -27,31 +27,36 @@ constexpr long long kAutoMaxParts = 32;
 constexpr long long kAutoPartitionFloor = 64;
 constexpr long long kAutoMinItems = 4096;
 constexpr long long kAutoSinglePass = 256;
-// Resident waves of the matrix-core kernel: 2 per SIMD on 256 CUs.
+// Resident waves of the matrix-core kernel on 256 CUs: 2 per SIMD, 3 for
+// its four-wave work-groups (at most 158 VGPRs, 32 KB of LDS per
+// work-group).
 constexpr long long kResidentWaves = 2048;
+long long resident_waves(int waves) { return waves == 4 ? 3072 : kResidentWaves; }
 
 // waves: waves per work-group (the matrix-core kernel runs ceil(G / 16)).
 // Measured with the longest-first item order: 1024-token partitions beat 512
 // by 2 % (mha_7b), 5 % (gqa_70b) and 8 % (multi-query, whose partial results
 // are G * D * 4 bytes per partition) and tie on gqa_long.
 // Wide groups (several waves per work-group) have few resident work-groups
-// (kResidentWaves / waves) and large partial results, so their partition
-// also doubles while the items (counted at the full table width) would not
-// all be resident at once: on the 256-sequence multi-query workload this
-// picks 2048 tokens at 64 heads (3353 vs 2998 GB/s at 1024) and keeps 1024
-// at 32 heads (3993 vs 3643 at 1536).
+// and large partial results, so their partition also doubles while the
+// items, counted at the full table width, would exceed a round of resident
+// waves by more than a third (batches rarely fill their tables).  On the
+// 256-sequence multi-query workload this keeps 1024 tokens at 64 heads
+// (cold step 83.0 / 84.6 us against 88.3 / 89.4 at 2048; 1280 gave 80.7 /
+// 83.2, 768 87.1 / 88.5) and at 32 heads (3993 vs 3643 GB/s at 1536).
 long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
     if (max_ctx <= kAutoSinglePass) return max_ctx;
     long long part = kAutoPartitionMin;
     while (part * kAutoMaxParts < max_ctx) part *= 2;
     const long long pairs = (long long)S * Hkv;
     auto items = [&](long long p) { return pairs * ((max_ctx + p - 1) / p); };
+    const long long resident = resident_waves(waves);
     if (waves > 1) {
-        while (part < max_ctx && items(part) * waves > kResidentWaves) part *= 2;
+        while (part < max_ctx && 3 * items(part) * waves > 4 * resident) part *= 2;
     }
     // small batches: cut finer until the items fill the machine (wide groups
     // settle for one round of resident waves)
-    const long long min_waves = waves > 1 ? kResidentWaves : kAutoMinItems;
+    const long long min_waves = waves > 1 ? resident : kAutoMinItems;
     while (part > kAutoPartitionFloor && items(part) * waves < min_waves) part /= 2;
     return part;
 }

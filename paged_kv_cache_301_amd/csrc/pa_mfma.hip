@@ -30,10 +30,24 @@ namespace {
 
 using namespace mfma;
 
+// Sub-tiles per iteration: W (each wave loads one), except for four waves
+// (64 heads), which load two sub-tiles between them, half a sub-tile each:
+// half the staging registers, score registers and LDS of one sub-tile per
+// wave, so 154 VGPRs and 32 KB of LDS give three waves per SIMD instead of
+// two (multi-query cold step 83-84 us against 90 at the partition each form
+// does best with).  Two waves (32 heads) sharing one sub-tile the same way
+// reach three waves per SIMD too (147 VGPRs) but ran slower (75-78 against
+// 72 us), so they keep one sub-tile each.
+constexpr int sub_tiles(int W) { return W == 4 ? 2 : W; }
+constexpr int waves_per_simd(int W) { return W == 4 ? 3 : 2; }
+
 template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
-__global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
+__global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)) void mfma_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
-    constexpr int W = (G + 15) / 16;          // waves per work-group = 32-token sub-tiles per iteration
+    constexpr int W = (G + 15) / 16;          // waves per work-group
+    constexpr int NS = sub_tiles(W);          // 32-token sub-tiles per iteration
+    constexpr int KL = kTileLoads * NS / W;   // load instructions per operand per wave
+    static_assert(KL * W == kTileLoads * NS && KL <= kTileLoads, "whole row quads per wave");
     int s, kvh, p;
     if (a.compact) {
         // 1-D grid over the live items, longest first (see pa_sched.h)
@@ -62,8 +76,8 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
     const int t_end = min(L, t_begin + a.part_tokens);
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
-    __shared__ uint4 klds[W][32 * 16];
-    __shared__ uint4 vlds[W][32 * 16];
+    __shared__ uint4 klds[NS][32 * 16];
+    __shared__ uint4 vlds[NS][32 * 16];
     __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
 
     // Q^T fragments of this wave's heads; columns past the group are zero
@@ -103,47 +117,51 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), 2) void mfma_kernel(Args a) {
             __syncthreads();
         }
 
-        constexpr int kIter = 32 * W;          // tokens per iteration
+        constexpr int kIter = 32 * NS;         // tokens per iteration
         const int niter = (t_end - t_begin + kIter - 1) / kIter;
-        const int tw = t_begin + 32 * w;       // this wave's sub-tile of iteration 0
+        // this wave's rows: quads KL w .. KL w + KL - 1 of the iteration, i.e.
+        // quads k0 .. k0 + KL - 1 of sub-tile u
+        const int u = KL * w / kTileLoads;
+        const int k0 = KL * w % kTileLoads;
+        const int tw = t_begin + 32 * u;       // this wave's sub-tile of iteration 0
         // One sub-tile of registers: as soon as this wave's sub-tile is in
         // LDS its registers take the loads of the next one, which stay in
         // flight through the barrier and both products.  (Holding two
         // register tiles and prefetching before the compute needs 223 VGPRs
         // instead of 184 and was 1-4 % slower.)  The scheduling barriers keep
         // the compiler from sinking that prefetch below the products.
-        KVTile tile;
+        KVTileN<KL> tile;
         if constexpr (SCALAR) {
-            ctx.load(tile, tw);
+            ctx.load(tile, tw, k0);
             for (int it = 0; it < niter; ++it) {
                 const int t0 = t_begin + kIter * it;
-                mfma_stage(tile, klds[w], vlds[w], g, i);
+                mfma_stage(tile, klds[u], vlds[u], g, i, k0);
                 __builtin_amdgcn_sched_barrier(0);
-                if (it + 1 < niter) ctx.load(tile, tw + kIter * (it + 1));   // uniform
+                if (it + 1 < niter) ctx.load(tile, tw + kIter * (it + 1), k0);   // uniform
                 __builtin_amdgcn_sched_barrier(0);
                 __syncthreads();   // every wave's rows visible
-                const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-                mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
+                const int nsub = min(NS, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
+                mfma_tiles<T, NS>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
                 __syncthreads();   // reads done before the next stage overwrites LDS
             }
         } else {
             // table in LDS (blocks of fewer than 4 tokens, one per row): the
             // next-but-one sub-tile's block ids are looked up while this one
             // is computed
-            int ids[kTileLoads];
-            ctx.ids(ids, tw);
-            ctx.load_ids(tile, ids, tw);
-            ctx.ids(ids, tw + kIter);
+            int ids[KL];
+            ctx.ids(ids, tw, k0);
+            ctx.load_ids(tile, ids, tw, k0);
+            ctx.ids(ids, tw + kIter, k0);
             for (int it = 0; it < niter; ++it) {
                 const int t0 = t_begin + kIter * it;
-                mfma_stage(tile, klds[w], vlds[w], g, i);
+                mfma_stage(tile, klds[u], vlds[u], g, i, k0);
                 __builtin_amdgcn_sched_barrier(0);
-                if (it + 1 < niter) ctx.load_ids(tile, ids, tw + kIter * (it + 1));   // uniform
+                if (it + 1 < niter) ctx.load_ids(tile, ids, tw + kIter * (it + 1), k0);   // uniform
                 __builtin_amdgcn_sched_barrier(0);
-                ctx.ids(ids, tw + kIter * (it + 2));
+                ctx.ids(ids, tw + kIter * (it + 2), k0);
                 __syncthreads();   // every wave's rows visible
-                const int nsub = min(W, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-                mfma_tiles<T, W>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
+                const int nsub = min(NS, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
+                mfma_tiles<T, NS>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
                 __syncthreads();   // reads done before the next stage overwrites LDS
             }
         }

@@ -160,12 +160,14 @@ struct MfmaState {
     float l;      // this lane's share of head i's weight sum
 };
 
-// This wave's tile rows 4k + g, chunk i, to its swizzled LDS images.
-__device__ __forceinline__ void mfma_stage(const KVTile &tile, uint4 *klds, uint4 *vlds, int g,
-                                           int i) {
+// This wave's tile rows 4 (k0 + k) + g, chunk i, k < N, to the swizzled LDS
+// images of their sub-tile.
+template <int N>
+__device__ __forceinline__ void mfma_stage(const KVTileN<N> &tile, uint4 *klds, uint4 *vlds,
+                                           int g, int i, int k0 = 0) {
 #pragma unroll
-    for (int k = 0; k < kTileLoads; ++k) {
-        const int row = 4 * k + g;
+    for (int k = 0; k < N; ++k) {
+        const int row = 4 * (k0 + k) + g;
         klds[row * 16 + (i ^ swz_k(row))] = tile.k[k];
         vlds[row * 16 + (i ^ swz_v(row))] = tile.v[k];
     }
