@@ -220,12 +220,20 @@ bool supports_prefill_mfma(int Hq, int Hkv, int D, int B, pa_dtype dt) {
 // holds fewer than one round of four-wave groups (two per CU).
 constexpr long long kPrefillMinGroups = 512;
 
-// Columns per work-group of the multi-token kernel: 64 (two waves) when
+// Columns per work-group of the multi-token kernel (32 per wave): 64 when
 // every sequence's rows fit them, so a 128-column block would be at least
-// half empty for every sequence; else 128.
+// half empty for every sequence; 256 when the longest chunk fills a
+// 256-column block, so each staged sub-tile serves twice the columns (half
+// the K / V re-reads of a sequence's query blocks); else 128.  Measured,
+// cold µs at 128 / 256 columns: 512 new tokens on the 16-sequence batch at 4
+// heads per kv head 1227 / 1169, at 8 heads 2157 / 1970, at 1 head 334 /
+// 330; 256 new tokens at 1 head (mha_7b batch) 995 / 919; at G x chunk =
+// 256 a tie (192 / 193).
 int prefill_columns(int G, int max_query_len) {
-    return (long long)G * max_query_len <= pa::kPrefillColumnsNarrow ? pa::kPrefillColumnsNarrow
-                                                                     : pa::kPrefillColumns;
+    const long long rows = (long long)G * max_query_len;
+    if (rows <= pa::kPrefillColumnsNarrow) return pa::kPrefillColumnsNarrow;
+    if (rows >= pa::kPrefillColumnsWide) return pa::kPrefillColumnsWide;
+    return pa::kPrefillColumns;
 }
 
 pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB, int max_blocks,

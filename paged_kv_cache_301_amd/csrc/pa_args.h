@@ -52,10 +52,12 @@ constexpr int kTableLds = 1024;
 constexpr int kSchedMaxSeqs = 1024;
 
 // (query token, head) columns per work-group of the multi-token matrix-core
-// kernel: four waves of two 16-column groups, or two waves when every
-// sequence's rows fit 64 columns (G * max_query_len <= 64).
+// kernel: four waves of two 16-column groups; two waves when every
+// sequence's rows fit 64 columns (G * max_query_len <= 64), eight when the
+// longest chunk fills 256 (G * max_query_len >= 256).
 constexpr int kPrefillColumns = 128;
 constexpr int kPrefillColumnsNarrow = 64;
+constexpr int kPrefillColumnsWide = 256;
 
 // Threads per work-group of the K / V write and block-copy kernels, and
 // bytes of one block one copy work-group moves.

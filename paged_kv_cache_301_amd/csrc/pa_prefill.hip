@@ -18,7 +18,11 @@
 // tokens, or one token of a wide group) the work-group has two waves and 64
 // columns instead, so no block is more than half empty by construction
 // (measured: 4 new tokens on the 16-sequence batch 104 -> 70 us, on the
-// 128-sequence 8-head-group batch 366 -> 334 us).  An iteration covers one
+// 128-sequence 8-head-group batch 366 -> 334 us).  When the longest chunk
+// fills 256 columns it has eight waves and 256 columns: each staged
+// sub-tile then serves twice the query rows, which halves the re-reads of
+// a sequence's context by its query blocks (HBM reads 2.2 -> 1.4 GB per
+// launch on the chunked-prefill batch) and ran 4-9 % faster.  An iteration covers one
 // 32-token sub-tile of whole K / V rows (pa_tile.h): each wave loads its
 // share of the rows, the shares meet in a double-buffered LDS image (one
 // barrier per iteration), and every wave reads the K and V^T fragments of the
@@ -161,8 +165,7 @@ __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
     }
 }
 
-// NW waves per work-group (4, or 2 when every sequence's rows fit 64
-// columns): 32 NW columns.
+// NW waves per work-group (2, 4 or 8; see kPrefillColumns): 32 NW columns.
 template <typename T, typename OutT, int G, int NW, bool SCALAR, bool STREAM>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
@@ -339,8 +342,12 @@ void launch_gw(const Args &a, hipStream_t st) {
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    if (a.prefill_columns == kPrefillColumnsNarrow) launch_gw<T, OutT, G, 2>(a, st);
-    else launch_gw<T, OutT, G, 4>(a, st);
+    switch (a.prefill_columns) {
+    case kPrefillColumnsNarrow: launch_gw<T, OutT, G, 2>(a, st); break;
+    case kPrefillColumns: launch_gw<T, OutT, G, 4>(a, st); break;
+    case kPrefillColumnsWide: launch_gw<T, OutT, G, 8>(a, st); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

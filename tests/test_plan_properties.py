@@ -10,8 +10,8 @@ planner accepts must satisfy what the kernels assume of it:
   1024 blocks;
 * one of the two decode grids (the 1-D live-item grid for at most 1024
   sequences, else the rectangular one) stays under the launch limit of 2^32
-  threads, and the multi-token grid likewise (128-column work-groups, or
-  64-column ones when every sequence's rows fit them);
+  threads, and the multi-token grid likewise (64-, 128- or 256-column
+  work-groups by the longest chunk);
 * a split plan's workspace holds every partial result (o, m, l in fp32);
 * an explicit partition is honoured unless it is not needed (one pass),
   too small for the grid or too large for the table slice.
@@ -33,6 +33,7 @@ SCHED_MAX_SEQS = 1024
 LAUNCH_LIMIT = 1 << 32
 PREFILL_COLUMNS = 128
 PREFILL_NARROW = 64
+PREFILL_WIDE = 256
 KERNELS = {"auto": b.KERNEL_AUTO, "generic": b.KERNEL_GENERIC, "valu": b.KERNEL_VALU,
            "mfma": b.KERNEL_MFMA}
 DTYPES = (b.PA_F32, b.PA_F16, b.PA_BF16)
@@ -205,8 +206,11 @@ def test_prefill_plan_properties(sh):
         assert ceil_div(P, B) <= TABLE_LDS
     # grid x: the (sequence, kv head) pairs padded to whole XCD rounds, times
     # the query blocks of cols / G tokens, 64 threads per 32 columns; cols is
-    # 64 when every sequence's rows fit them, else 128
-    cols = PREFILL_NARROW if sh["G"] * sh["mql"] <= PREFILL_NARROW else PREFILL_COLUMNS
+    # 64 when every sequence's rows fit them, 256 when the longest chunk
+    # fills 256, else 128
+    rows = sh["G"] * sh["mql"]
+    cols = (PREFILL_NARROW if rows <= PREFILL_NARROW
+            else PREFILL_WIDE if rows >= PREFILL_WIDE else PREFILL_COLUMNS)
     qb = ceil_div(sh["mql"], cols // sh["G"])
     assert ceil_div(S * Hkv, 8) * 8 * qb * 2 * cols < LAUNCH_LIMIT
     if p.split:
