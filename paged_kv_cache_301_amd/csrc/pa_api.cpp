@@ -106,10 +106,22 @@ long long table_cap(int kernel, int B) {
     return staged ? (long long)pa::kTableLds * B : (long long)INT_MAX;
 }
 
+// Waves per item of the VALU kernel: each wave streams every NW-th 32-token
+// tile of the partition, so a long partition runs on up to four waves, about
+// 1024 tokens each, and their softmax states meet in LDS.  Blocks of fewer
+// than 4 tokens keep one wave (their partitions are capped by the LDS table
+// slice anyway).
+int valu_waves(long long part, int B) {
+    if (B % 4 != 0) return 1;
+    return part >= 4096 ? 4 : part >= 2048 ? 2 : 1;
+}
+
 // Threads per work-group of a decode kernel family (the matrix-core kernel
-// runs ceil(G / 16) waves).
-int decode_threads(int kernel, int G) {
-    return kernel == PA_KERNEL_MFMA ? 64 * ((G + 15) / 16) : 64;
+// runs ceil(G / 16) waves, the VALU kernel valu_waves).
+int decode_threads(int kernel, int G, long long part, int B) {
+    if (kernel == PA_KERNEL_MFMA) return 64 * ((G + 15) / 16);
+    if (kernel == PA_KERNEL_VALU) return 64 * valu_waves(part, B);
+    return 64;
 }
 
 // Grid of the tiled decode kernels: 1 = the 1-D live-item grid (every
@@ -159,6 +171,18 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
         const long long cap = table_cap(kernel, B);
         const int waves = kernel == PA_KERNEL_MFMA ? (Hq / Hkv + 15) / 16 : 1;
         long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx, waves);
+        // VALU kernel: a full one-wave partition (not one halved for a small
+        // batch) becomes four waves on a partition four times as long, each
+        // wave streaming as many tokens as before, with a quarter of the
+        // partial results (none when that covers the context).  Cold step
+        // µs, one wave -> four: batch-64 MHA 358.7 -> 347.0, at two heads
+        // per kv head 373.4 -> 352.4, 256 sequences 1519 -> 1450, 32
+        // sequences 192.2 -> 186.7, 16 long contexts 209.0 -> 206.9; a
+        // partition halved for a small batch stays on one wave (8 sequences
+        // of up to 2048 tokens: 27.3 against 29.4-31.8 on four).
+        if (req == 0 && kernel == PA_KERNEL_VALU && B % 4 == 0 && part >= kAutoPartitionMin &&
+            part < max_ctx)
+            part *= 4;
         if (part >= max_ctx) {   // single pass: one partition covers any context
             part = ((max_ctx > 0 ? max_ctx : 1) + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;
         }
@@ -186,7 +210,8 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
         p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
         p.max_partitions = 1;
         p.split = 0;
-    } else if (decode_grid_mode(S, Hkv, p.max_partitions, decode_threads(kernel, Hq / Hkv)) < 0) {
+    } else if (decode_grid_mode(S, Hkv, p.max_partitions,
+                                decode_threads(kernel, Hq / Hkv, p.partition_tokens, B)) < 0) {
         return PA_ERR_SHAPE;
     }
     if (p.split) {
@@ -387,9 +412,11 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     // live-item grid when every work-group can decode its item from the
     // lengths held in one wave's registers and the 1-D grid fits (the plan
     // has checked that one of the two grids fits)
+    a.valu_waves = plan.kernel == PA_KERNEL_VALU ? valu_waves(plan.partition_tokens, B) : 1;
     a.compact = plan.kernel != PA_KERNEL_GENERIC &&
                 decode_grid_mode(S, Hkv, plan.max_partitions,
-                                 decode_threads(plan.kernel, Hq / Hkv)) == 1;
+                                 decode_threads(plan.kernel, Hq / Hkv, plan.partition_tokens,
+                                                B)) == 1;
     if (plan.split) {
         const size_t rows = (size_t)S * Hq * plan.max_partitions;
         char *ws = static_cast<char *>(workspace);

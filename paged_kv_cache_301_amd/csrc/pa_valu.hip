@@ -99,8 +99,13 @@ __device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const KVTile &
     }
 }
 
-template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
-__global__ __launch_bounds__(64) void valu_kernel(Args a) {
+// NW waves per item (1, 2 or 4 by the partition's length): wave w runs the
+// item's 32-token tiles w, w + NW, ..., and the waves' softmax states meet
+// in LDS at the end.  Long partitions on several waves need a quarter of the
+// partial results of short ones on one, or none when a partition covers the
+// whole context.
+template <typename T, typename OutT, int G, int NW, bool SCALAR, bool STREAM>
+__global__ __launch_bounds__(64 * NW) void valu_kernel(Args a) {
     int s, kvh, p;
     if (a.compact) {
         // 1-D grid over the live items, longest first (see pa_sched.h)
@@ -118,7 +123,8 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         s = blockIdx.x / a.Hkv;
         p = blockIdx.y;
     }
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane & 15;
     const int g = lane >> 4;
 
@@ -129,6 +135,8 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
     __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
+    // the other waves' states, lanes 0..15 of each: m, l and 8 output columns
+    __shared__ float xst[NW > 1 ? NW - 1 : 1][G][16][10];
 
     uint4 q[G];
 #pragma unroll
@@ -159,13 +167,17 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         ctx.tv.j0 = t_begin >> a.log2B;
         ctx.tbl = tbl;
         if constexpr (!SCALAR) {
-            stage_table<64>(tbl, ctx.tv, t_begin, t_end, lane);
+            stage_table<64 * NW>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
             __syncthreads();
         }
 
-        const int niter = (t_end - t_begin + 31) >> 5;
+        // this wave's tiles: w, w + NW, ... of the partition's 32-token tiles
+        const int ntiles = (t_end - t_begin + 31) >> 5;
+        const int niter = (ntiles - w + NW - 1) / NW;
+        constexpr int kStep = 32 * NW;
+        const int tw = t_begin + 32 * w;
         KVTile ta, tb;
-        ctx.load(ta, t_begin);
+        ctx.load(ta, tw);
         // The scheduling barriers keep each prefetch ahead of the wait for
         // the tile computed next; without them the compiler sinks the loads
         // below that wait and the wave never has two tiles in flight.  The
@@ -174,14 +186,14 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         // kernel from 159 to 206 VGPRs, two waves per SIMD instead of three,
         // and was slower.
         for (int it = 0; it < niter; it += 2) {
-            const int t0 = t_begin + 32 * it;
-            ctx.load(tb, t0 + 32);
+            const int t0 = tw + kStep * it;
+            ctx.load(tb, t0 + kStep);
             __builtin_amdgcn_sched_barrier(0);
             valu_compute<T, G>(st, ta, q, t0, t_end, g, a.scale_log2);
             __builtin_amdgcn_sched_barrier(0);
-            ctx.load(ta, t0 + 64);
+            ctx.load(ta, t0 + 2 * kStep);
             __builtin_amdgcn_sched_barrier(0);
-            if (it + 1 < niter) valu_compute<T, G>(st, tb, q, t0 + 32, t_end, g, a.scale_log2);
+            if (it + 1 < niter) valu_compute<T, G>(st, tb, q, t0 + kStep, t_end, g, a.scale_log2);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -200,6 +212,35 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
         }
     }
 
+    if constexpr (NW > 1) {
+        // the other waves hand their states to wave 0 (L and the partition
+        // are the work-group's, so every wave reaches the barrier)
+        if (w > 0 && g == 0) {
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                float *x = xst[w - 1][i][c];
+                x[0] = st.m[i];
+                x[1] = st.l[i];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[2 + e] = st.o[i][e];
+            }
+        }
+        __syncthreads();
+        if (w > 0) return;
+        if (g == 0) {
+#pragma unroll
+            for (int u = 0; u < NW - 1; ++u) {
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const float *x = xst[u][i][c];
+                    float o2[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o2[e] = x[2 + e];
+                    merge_state(st.m[i], st.l[i], st.o[i], 8, x[0], x[1], o2);
+                }
+            }
+        }
+    }
     if (g != 0) return;
     if (nparts <= 1) {
 #pragma unroll
@@ -224,18 +265,26 @@ __global__ __launch_bounds__(64) void valu_kernel(Args a) {
     }
 }
 
-template <typename T, typename OutT, int G>
-hipError_t launch_g(const Args &a, hipStream_t st) {
+template <typename T, typename OutT, int G, int NW>
+void launch_gw(const Args &a, hipStream_t st) {
     const dim3 grid = a.compact ? dim3((unsigned)((long long)a.Hkv * a.S * a.max_parts))
                                 : dim3(a.Hkv * a.S, a.max_parts);
+    const dim3 block(64 * NW);
     const bool scalar = a.B % 4 == 0;
     if (a.stream_kv) {
-        if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, true, true>), grid, dim3(64), 0, st, a);
-        else hipLaunchKernelGGL((valu_kernel<T, OutT, G, false, true>), grid, dim3(64), 0, st, a);
+        if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, NW, true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((valu_kernel<T, OutT, G, NW, false, true>), grid, block, 0, st, a);
     } else {
-        if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, true, false>), grid, dim3(64), 0, st, a);
-        else hipLaunchKernelGGL((valu_kernel<T, OutT, G, false, false>), grid, dim3(64), 0, st, a);
+        if (scalar) hipLaunchKernelGGL((valu_kernel<T, OutT, G, NW, true, false>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((valu_kernel<T, OutT, G, NW, false, false>), grid, block, 0, st, a);
     }
+}
+
+template <typename T, typename OutT, int G>
+hipError_t launch_g(const Args &a, hipStream_t st) {
+    if (a.valu_waves == 4) launch_gw<T, OutT, G, 4>(a, st);
+    else if (a.valu_waves == 2) launch_gw<T, OutT, G, 2>(a, st);
+    else launch_gw<T, OutT, G, 1>(a, st);
     return hipGetLastError();
 }
 

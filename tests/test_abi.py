@@ -71,11 +71,19 @@ def test_empty_batch_is_noop(lib):
 
 
 def test_plans():
-    # one head per kv head: the VALU kernel unless the matrix cores are asked for
+    # one head per kv head: the VALU kernel unless the matrix cores are asked
+    # for; a full 1024-token partition becomes four waves on 4096 tokens,
+    # here the whole context (one pass, no workspace)
     p = b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16)
-    assert p["kernel"] == b.KERNEL_VALU and p["split"] == 1 and p["partition_tokens"] == 1024
-    assert p["max_partitions"] * p["partition_tokens"] >= 256 * 16
+    assert p["kernel"] == b.KERNEL_VALU and p["split"] == 0 and p["partition_tokens"] == 4096
+    assert p["workspace_bytes"] == 0
+    p = b.plan(64, 32, 32, 128, 16, 15360, 1024, torch.bfloat16)     # 16k-token tables
+    assert p["split"] == 1 and p["partition_tokens"] == 4096 and p["max_partitions"] == 4
     assert p["workspace_bytes"] >= 64 * 32 * p["max_partitions"] * (128 + 2) * 4
+    # a partition halved for a small batch, or one-token blocks, stay on one wave
+    assert b.plan(8, 32, 32, 128, 16, 15360, 128, torch.bfloat16)["partition_tokens"] == 128
+    p = b.plan(64, 32, 32, 128, 1, 300000, 4096, torch.bfloat16)
+    assert p["partition_tokens"] <= 1024
     assert b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16,
                   kernel="mfma")["kernel"] == b.KERNEL_MFMA
     assert b.plan(8, 16, 8, 128, 16, 645, 128, torch.float16)["kernel"] == b.KERNEL_VALU

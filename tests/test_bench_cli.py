@@ -67,16 +67,22 @@ def test_traffic_records_are_well_formed():
         seen.add(key)
 
 
-@pytest.mark.parametrize("kernel,workload,B,P", [
-    ("pa_valu_partitions", "mha_7b", 16, 1024),
-    ("pa_mfma_partitions", "gqa_70b", 16, 1024),
-    ("pa_mfma_partitions", "gqa_long", 16, 1024),
+@pytest.mark.parametrize("kernel,workload,B", [
+    ("pa_valu_partitions", "mha_7b", 16),
+    ("pa_mfma_partitions", "gqa_70b", 16),
+    ("pa_mfma_partitions", "gqa_long", 16),
 ])
-def test_headline_workloads_have_current_records(kernel, workload, B, P):
+def test_headline_workloads_have_current_records(kernel, workload, B):
     """The decode workloads the targets name carry HBM traffic measured on the
-    current kernel sources.  After a kernel change the records are stale until
-    the profiles are taken again: reported as a skip naming the record (the
-    bench line then reports traffic null), not as a failure."""
+    current kernel sources, at the partition the automatic plan picks.  After
+    a kernel change the records are stale until the profiles are taken again:
+    reported as a skip naming the record (the bench line then reports traffic
+    null), not as a failure."""
+    from paged_kv_cache_301_amd import binding, workloads
+    sp = workloads.SPECS[workload].replace(B=B)
+    max_blocks = (sp.max_len + B - 1) // B
+    P = binding.plan(sp.S, sp.Hq, sp.Hkv, sp.D, B, 1 << 20, max_blocks,
+                     workloads._DTYPES[sp.dtype])["partition_tokens"]
     assert any(r[1:5] == (kernel, workload, str(B), str(P)) for r in records()), \
         f"no record at all for {kernel} {workload} B={B} P={P}"
     got = bench.recorded_traffic(kernel, workload, B, P)

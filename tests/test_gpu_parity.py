@@ -519,3 +519,32 @@ def test_pool_beyond_4gib_small_blocks(kernel, Hq, Hkv, B):
     assert torch.equal(a, b), "moving blocks beyond 4 GiB changed the output"
     del big_k, big_v
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- VALU kernel: waves per item
+
+@pytest.mark.parametrize("Hq,Hkv,B,part", [(8, 8, 16, 2048), (8, 8, 16, 4096), (16, 8, 4, 4096),
+                                           (8, 8, 16, 8192), (16, 8, 16, 2048), (8, 8, 32, 4096)])
+def test_valu_waves_per_item(Hq, Hkv, B, part):
+    """Partitions of 2048 (4096 and more) tokens run on two (four) waves of
+    one work-group, each streaming every second (fourth) 32-token tile, their
+    softmax states merged in LDS; a partition covering the context is one
+    pass.  Every row against the oracle, the workspace NaN-filled, with
+    empty, one-tile and ragged contexts."""
+    say(f"case: VALU waves per item Hq={Hq} Hkv={Hkv} B={B} part={part}")
+    lens = (1, 33, 1000, 4096, 5000, 2047, 0, 8191)
+    spec = workloads.WorkloadSpec("valu_waves", S=len(lens), Hq=Hq, Hkv=Hkv, D=128, B=B,
+                                  dtype="bf16", lens=("fixed", lens), max_len=8192,
+                                  pool=("free", 0.2), seed=700 + part // 1024 + B)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, kernel="valu",
+                     partition_tokens=part)
+    assert p["kernel"] == binding.KERNEL_VALU and p["partition_tokens"] == part
+    ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+          if p["workspace_bytes"] else None)
+    ref = oracle_full(w)
+    out = run(w, out_dtype=torch.float32, kernel="valu", partition_tokens=part, workspace=ws)
+    check(out, ref, torch.bfloat16, f"valu waves part={part}")
+    assert torch.equal(out[6], torch.zeros_like(out[6]))
+    check(run(w, kernel="valu", partition_tokens=part, workspace=ws), ref, torch.bfloat16,
+          f"valu waves part={part}/native")

@@ -131,7 +131,10 @@ def test_decode_plan_properties(sh):
     assert p.split == (1 if parts > 1 else 0)
     if B % 4 != 0:
         assert ceil_div(P, B) <= TABLE_LDS
-    threads = 64 * ceil_div(Hq // Hkv, 16) if p.kernel == b.KERNEL_MFMA else 64
+    if p.kernel == b.KERNEL_MFMA:
+        threads = 64 * ceil_div(Hq // Hkv, 16)
+    else:   # VALU: 1, 2 or 4 waves per item by the partition's length
+        threads = 64 * (1 if B % 4 else 4 if P >= 4096 else 2 if P >= 2048 else 1)
     compact = S <= SCHED_MAX_SEQS and S * Hkv * parts * threads < LAUNCH_LIMIT
     rect = S * Hkv * threads < LAUNCH_LIMIT and parts <= MAX_PARTS
     assert compact or rect
