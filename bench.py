@@ -73,6 +73,8 @@ def parse():
                     help="every sequence this many tokens (a uniform batch; the table fits it)")
     ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--token-waves", type=int, default=0, choices=[0, 1, 2, 4],
+                    help="waves per decode item (0: the planner's choice)")
     ap.add_argument("--kv-reuse", choices=["on", "off"], default="off",
                     help="cached (on) or streamed (off, default) K/V loads")
     ap.add_argument("--graph", action="store_true",
@@ -157,22 +159,25 @@ def record_key(workload: str, args) -> str:
     return key
 
 
-def recorded_traffic(kernel: str, workload: str, block_size: int, partition: int = 0):
+def recorded_traffic(kernel: str, workload: str, block_size: int, partition: int = 0,
+                     token_waves: int = 1):
     """HBM bytes per launch from a rocprofv3 --pmc summary under profiles/,
-    if one was recorded for these exact kernel sources and the same partition
-    size (0: the kernel has none); else None."""
+    if one was recorded for these exact kernel sources, the same partition
+    size (0: the kernel has none) and the same waves per decode item; else
+    None."""
     import glob
     import re
     if kernel not in KERNEL_SOURCES:
         return None
     sha = source_sha256(kernel)
-    pat = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) P=(\d+) "
+    pat = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) P=(\d+) TW=(\d+) "
                      r"source_sha256=([0-9a-f]+) read_bytes=(\d+) write_bytes=(\d+)")
-    want = (kernel, workload, block_size, partition, sha)
+    want = (kernel, workload, block_size, partition, token_waves, sha)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for m in pat.finditer(open(path).read()):
-            if (m.group(1), m.group(2), int(m.group(3)), int(m.group(4)), m.group(5)) == want:
-                return int(m.group(6)) + int(m.group(7))
+            if (m.group(1), m.group(2), int(m.group(3)), int(m.group(4)), int(m.group(5)),
+                    m.group(6)) == want:
+                return int(m.group(7)) + int(m.group(8))
     return None
 
 
@@ -229,20 +234,21 @@ def stats_us(ms):
             "p90_us": round(float(np.percentile(a, 90)), 2)}
 
 
-def measure_decode(w, args, dev, scratch, kernel="auto", partition_tokens=0, kv_reuse=False):
+def measure_decode(w, args, dev, scratch, kernel="auto", partition_tokens=0, kv_reuse=False,
+                   token_waves=0):
     """Cold-cache and warm timings of one decode workload (see the module
     docstring).  Returns (plan, timing dict, prepared step callables)."""
     import torch
     from paged_kv_cache_301_amd import binding
     plan = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype,
-                        kernel=kernel, partition_tokens=partition_tokens)
+                        kernel=kernel, partition_tokens=partition_tokens, token_waves=token_waves)
     ws = None
     if plan["workspace_bytes"]:
         ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=dev)
     out = torch.empty_like(w.query)
     stream = torch.cuda.current_stream(dev)
     kw = dict(kernel=kernel, partition_tokens=partition_tokens, workspace=ws, stream=stream,
-              kv_reuse=kv_reuse)
+              kv_reuse=kv_reuse, token_waves=token_waves)
     args_ = (w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale, out)
     run_parts = binding.prepare(*args_, stages=binding.STAGE_PARTITIONS, **kw)
     run_combine = binding.prepare(*args_, stages=binding.STAGE_COMBINE, **kw)
@@ -303,7 +309,7 @@ def decode_summary(w, plan, t, kname, floor=None):
         "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "B": w.B,
         "tokens": int(w.lens.sum()), "kv_bytes": kv, "unique_kv_bytes": unique,
         "kernel": kname, "partition_tokens": plan["partition_tokens"], "split": bool(plan["split"]),
-        "step_cold_us": t["cold"], "kernel_cold_us": t["partitions"],
+        "token_waves": plan["token_waves"], "step_cold_us": t["cold"], "kernel_cold_us": t["partitions"],
         "combine_cold_us": t["combine"], "warm": t["warm"],
         "gbs": round(kv / step_s / 1e9, 2), "hbm_frac": round(kv / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "unique_gbs": round(unique / step_s / 1e9, 2),
@@ -636,7 +642,7 @@ def main():
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # cache eviction
     plan, t, (step, args_, kw) = measure_decode(w, args, dev, scratch, kernel=args.kernel,
                                                 partition_tokens=args.partition_tokens,
-                                                kv_reuse=kv_reuse)
+                                                kv_reuse=kv_reuse, token_waves=args.token_waves)
     kname = KERNEL_NAMES[plan["kernel"]]
     uniq0 = w.unique_kv_bytes() if w.spec.prefix_tokens else w.kv_bytes()
     floor = None if args.no_read_peak else plain_read_floor(uniq0, args, dev, scratch)
@@ -676,7 +682,7 @@ def main():
     extra = None
     if not args.no_extra_configs and not (args.block_size or args.q_heads or args.seqs
                                           or args.fixed_len or args.kernel != "auto"
-                                          or args.partition_tokens):
+                                          or args.partition_tokens or args.token_waves):
         extra = {}
         for key, name, over in (("mha_small", "mha_small", {}), ("gqa_70b", "gqa_70b", {}),
                                 ("gqa_long_B16", "gqa_long", {"B": 16})):
@@ -719,7 +725,7 @@ def main():
                    "B": w.B, "tokens": int(w.lens.sum()), "kv_bytes": kv,
                    "unique_kv_bytes": unique or kv,
                    "kernel": kname, "partition_tokens": plan["partition_tokens"],
-                   "kv_reuse": kv_reuse, "fixed_len": args.fixed_len,
+                   "token_waves": plan["token_waves"], "kv_reuse": kv_reuse, "fixed_len": args.fixed_len,
                    "split": bool(plan["split"]), "timing": "cold cache, median step"},
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(w.S / (step_ms * 1e-3), 1),
@@ -741,7 +747,7 @@ def main():
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"pa_{kname}_partitions", record_key(args.workload, args), w.B,
-                                                 plan["partition_tokens"])},
+                                                 plan["partition_tokens"], plan["token_waves"])},
         "configs": extra,
     }
     if not args.no_read_peak:

@@ -122,6 +122,16 @@ typedef struct {
     int check;            /* checked mode: 0 follows the PA_CHECK environment
                              variable (on when it is "1"), 1 always checks,
                              -1 never checks.  See pa_get_device_error.          */
+    int token_waves;      /* 0: automatic.  1, 2 or 4: waves of one work-group
+                             that share each (sequence, kv head, partition)
+                             item's tokens, every one streaming every
+                             token_waves-th 32-token tile, their softmax
+                             states merged in LDS.  Above 1 it needs the VALU
+                             kernel or the matrix-core kernel with at most 16
+                             query heads per kv head, and a block size that is
+                             a multiple of 4 (else PA_ERR_UNSUPPORTED); other
+                             values are PA_ERR_SHAPE.  Decode only: the
+                             multi-token calls accept 0 or 1.                   */
 } pa_config;
 
 /* The plan a call will execute (filled by pa_decode_plan). */
@@ -133,6 +143,7 @@ typedef struct {
                              combine stage merges them; 0: single pass          */
     size_t workspace_bytes; /* bytes of device workspace the plan needs (0 if
                                single pass)                                     */
+    int token_waves;      /* waves per item (1, 2 or 4; see pa_config)          */
 } pa_plan;
 
 /*

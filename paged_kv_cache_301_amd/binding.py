@@ -38,13 +38,14 @@ _TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA
 
 class PaConfig(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("partition_tokens", ctypes.c_int),
-                ("stages", ctypes.c_int), ("kv_reuse", ctypes.c_int), ("check", ctypes.c_int)]
+                ("stages", ctypes.c_int), ("kv_reuse", ctypes.c_int), ("check", ctypes.c_int),
+                ("token_waves", ctypes.c_int)]
 
 
 class PaPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("partition_tokens", ctypes.c_int),
                 ("max_partitions", ctypes.c_int), ("split", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("token_waves", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -159,18 +160,24 @@ def _check_flag(check) -> int:
     return 0 if check is None else (1 if check else -1)
 
 
-def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, check=None) -> PaConfig:
+def _config(kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, check=None,
+            token_waves=None) -> PaConfig:
     """The C config.  Choices left to the library (kernel "auto", partition 0)
     take the PA_KERNEL (auto / generic / valu / mfma) and PA_PARTITION_TOKENS
-    environment variables when those are set; explicit arguments win."""
+    environment variables when those are set, and decode token-waves (None)
+    PA_TOKEN_WAVES; explicit arguments win.  The multi-token calls pass
+    token_waves=0."""
     if isinstance(kernel, str) and kernel == "auto":
         kernel = os.environ.get("PA_KERNEL", "auto") or "auto"
     if not partition_tokens:
         partition_tokens = int(os.environ.get("PA_PARTITION_TOKENS", "0") or 0)
+    if token_waves is None:
+        token_waves = int(os.environ.get("PA_TOKEN_WAVES", "0") or 0)
     if isinstance(kernel, str) and kernel not in KERNELS:
         raise ValueError(f"unknown kernel {kernel!r} (one of {sorted(KERNELS)})")
     k = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    return PaConfig(k, int(partition_tokens), int(stages), int(bool(kv_reuse)), _check_flag(check))
+    return PaConfig(k, int(partition_tokens), int(stages), int(bool(kv_reuse)), _check_flag(check),
+                    int(token_waves))
 
 
 def _shape_args(query, key_cache, block_tables, out_dtype):
@@ -183,12 +190,12 @@ def _shape_args(query, key_cache, block_tables, out_dtype):
 
 
 def plan(S, Hq, Hkv, D, B, NB, max_blocks, dtype, out_dtype=None, *, kernel="auto",
-         partition_tokens=0, stages=0, kv_reuse=False) -> dict:
+         partition_tokens=0, stages=0, kv_reuse=False, token_waves=None) -> dict:
     """Resolve the plan for a shape (host only; no GPU needed)."""
     dt = _TORCH_TO_PA.get(dtype, dtype)
     odt = dt if out_dtype is None else _TORCH_TO_PA.get(out_dtype, out_dtype)
     p = PaPlan()
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, token_waves=token_waves)
     _check(load().pa_decode_plan(S, Hq, Hkv, D, B, NB, max_blocks, dt, odt,
                                  ctypes.byref(cfg), ctypes.byref(p)))
     return p.as_dict()
@@ -199,7 +206,7 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
            out: Optional[torch.Tensor] = None, *, out_dtype: Optional[torch.dtype] = None,
            kernel="auto", partition_tokens: int = 0, stages: int = 0, kv_reuse: bool = False,
            workspace: Optional[torch.Tensor] = None, stream=None,
-           check: Optional[bool] = None) -> torch.Tensor:
+           check: Optional[bool] = None, token_waves: Optional[int] = None) -> torch.Tensor:
     """Paged decode attention: out[S,Hq,D] from query[S,Hq,D], K/V pools
     [NB,Hkv,B,D], block_tables[S,max_blocks] int32 and seq_lens[S] int32.
 
@@ -232,7 +239,7 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
     shape = _shape_args(query, key_cache, block_tables, out_dtype)
     if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
         raise ValueError("seq_lens / block_tables do not match the batch size")
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check, token_waves)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
     tstream = _torch_stream(stream, query.device)
@@ -255,7 +262,7 @@ def decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tens
 
 def decode_noalloc(query, key_cache, value_cache, block_tables, seq_lens, scale, out, *,
                    kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, stream=None,
-                   check: Optional[bool] = None) -> torch.Tensor:
+                   check: Optional[bool] = None, token_waves: Optional[int] = None) -> torch.Tensor:
     """``decode`` through pa_decode_noalloc: the split plan's partial results
     go to the library's static device scratch, and nothing is allocated here
     either (``out`` must be given).  Calls that overlap on one GPU race for
@@ -274,7 +281,7 @@ def decode_noalloc(query, key_cache, value_cache, block_tables, seq_lens, scale,
     shape = _shape_args(query, key_cache, block_tables, out.dtype)
     if seq_lens.shape != (shape[0],) or block_tables.shape[0] != shape[0]:
         raise ValueError("seq_lens / block_tables do not match the batch size")
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check, token_waves)
     _check(lib.pa_decode_noalloc(query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
                                  block_tables.data_ptr(), seq_lens.data_ptr(), float(scale),
                                  out.data_ptr(), *shape, ctypes.byref(cfg),
@@ -288,7 +295,7 @@ def plan_prefill(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dtype, out_
     dt = _TORCH_TO_PA.get(dtype, dtype)
     odt = dt if out_dtype is None else _TORCH_TO_PA.get(out_dtype, out_dtype)
     p = PaPlan()
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, token_waves=0)
     _check(load().pa_prefill_plan(S, T, Hq, Hkv, D, B, NB, max_blocks, max_query_len, dt, odt,
                                   ctypes.byref(cfg), ctypes.byref(p)))
     return p.as_dict()
@@ -336,7 +343,7 @@ def prefill(query, key_cache, value_cache, block_tables, seq_lens, query_start, 
         raise ValueError("out must be a contiguous [T,Hq,D] tensor of out_dtype")
     shape = (S, T, Hq, Hkv, D, B, NB, block_tables.shape[1], int(max_query_len),
              _TORCH_TO_PA[query.dtype], _TORCH_TO_PA[out_dtype])
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check, 0)
     p = PaPlan()
     _check(lib.pa_prefill_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
     tstream = _torch_stream(stream, query.device)
@@ -587,13 +594,14 @@ class PreparedCall:
 
 def prepare(query, key_cache, value_cache, block_tables, seq_lens, scale, out, *,
             kernel="auto", partition_tokens=0, stages=0, kv_reuse=False, workspace=None,
-            stream=None, check: Optional[bool] = None) -> PreparedCall:
+            stream=None, check: Optional[bool] = None,
+            token_waves: Optional[int] = None) -> PreparedCall:
     """Validate once (by running the same checks as ``decode`` on a plan) and
     return a PreparedCall that launches the configured stage(s).  ``check``
     as in ``decode``: the library's device check then runs at every call."""
     lib = load()
     shape = _shape_args(query, key_cache, block_tables, out.dtype)
-    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check)
+    cfg = _config(kernel, partition_tokens, stages, kv_reuse, check, token_waves)
     p = PaPlan()
     _check(lib.pa_decode_plan(*shape, ctypes.byref(cfg), ctypes.byref(p)))
     if p.workspace_bytes and workspace is None:

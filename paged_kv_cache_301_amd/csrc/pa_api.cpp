@@ -27,6 +27,9 @@ constexpr long long kAutoMaxParts = 32;
 constexpr long long kAutoPartitionFloor = 64;
 constexpr long long kAutoMinItems = 4096;
 constexpr long long kAutoSinglePass = 256;
+// (sequence, kv head) pairs from which the automatic plan runs items on
+// four token-waves (see make_plan).
+constexpr long long kMultiWavePairs = 512;
 // Resident waves of the matrix-core kernel on 256 CUs: 2 per SIMD, 3 for
 // its four-wave work-groups (at most 158 VGPRs, 32 KB of LDS per
 // work-group).
@@ -106,21 +109,25 @@ long long table_cap(int kernel, int B) {
     return staged ? (long long)pa::kTableLds * B : (long long)INT_MAX;
 }
 
-// Waves per item of the VALU kernel: each wave streams every NW-th 32-token
-// tile of the partition, so a long partition runs on up to four waves, about
-// 1024 tokens each, and their softmax states meet in LDS.  Blocks of fewer
+// Token-waves per item of the VALU kernel and of the matrix-core kernel's
+// one-wave groups (at most 16 heads): each streams every TW-th 32-token tile
+// of the partition, and their softmax states meet in LDS.  Blocks of fewer
 // than 4 tokens keep one wave (their partitions are capped by the LDS table
 // slice anyway).
-int valu_waves(long long part, int B) {
-    if (B % 4 != 0) return 1;
-    return part >= 4096 ? 4 : part >= 2048 ? 2 : 1;
+bool multi_wave_items(int kernel, int G, int B) {
+    return (kernel == PA_KERNEL_VALU || (kernel == PA_KERNEL_MFMA && G <= 16)) && B % 4 == 0;
 }
 
+// Waves for a partition the planner made multi-wave: about 1024 tokens or
+// more each (a single-pass partition cut to the longest context can be
+// shorter than the four-fold one).
+int waves_for_length(long long part) { return part >= 4096 ? 4 : part >= 2048 ? 2 : 1; }
+
 // Threads per work-group of a decode kernel family (the matrix-core kernel
-// runs ceil(G / 16) waves, the VALU kernel valu_waves).
-int decode_threads(int kernel, int G, long long part, int B) {
-    if (kernel == PA_KERNEL_MFMA) return 64 * ((G + 15) / 16);
-    if (kernel == PA_KERNEL_VALU) return 64 * valu_waves(part, B);
+// runs ceil(G / 16) head waves, times its token-waves).
+int decode_threads(int kernel, int G, int tw) {
+    if (kernel == PA_KERNEL_MFMA) return 64 * ((G + 15) / 16) * tw;
+    if (kernel == PA_KERNEL_VALU) return 64 * tw;
     return 64;
 }
 
@@ -143,6 +150,8 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
     const int req = cfg ? cfg->partition_tokens : 0;
     if (req < 0 || (req > 0 && req % pa::kTileTokens != 0)) return PA_ERR_SHAPE;
     if (cfg && (cfg->stages < 0 || cfg->stages > PA_STAGE_ALL)) return PA_ERR_SHAPE;
+    const int req_tw = cfg ? cfg->token_waves : 0;
+    if (req_tw != 0 && req_tw != 1 && req_tw != 2 && req_tw != 4) return PA_ERR_SHAPE;
 
     switch (kernel) {
     case PA_KERNEL_AUTO:
@@ -165,24 +174,36 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
         return PA_ERR_UNSUPPORTED;
     }
 
+    const int G = Hq / Hkv;
+    if (req_tw > 1 && !multi_wave_items(kernel, G, B)) return PA_ERR_UNSUPPORTED;
     const long long max_ctx = (long long)max_blocks * B;
     pa_plan p{};
+    bool multi = false;   // the planner chose multi-wave items
     if (kernel != PA_KERNEL_GENERIC) {
         const long long cap = table_cap(kernel, B);
         const int waves = kernel == PA_KERNEL_MFMA ? (Hq / Hkv + 15) / 16 : 1;
         long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx, waves);
-        // VALU kernel: a full one-wave partition (not one halved for a small
+        // Token-waves: with at least kMultiWavePairs (sequence, kv head)
+        // pairs, a full one-wave partition (not one halved for a small
         // batch) becomes four waves on a partition four times as long, each
         // wave streaming as many tokens as before, with a quarter of the
         // partial results (none when that covers the context).  Cold step
-        // µs, one wave -> four: batch-64 MHA 358.7 -> 347.0, at two heads
-        // per kv head 373.4 -> 352.4, 256 sequences 1519 -> 1450, 32
-        // sequences 192.2 -> 186.7, 16 long contexts 209.0 -> 206.9; a
-        // partition halved for a small batch stays on one wave (8 sequences
-        // of up to 2048 tokens: 27.3 against 29.4-31.8 on four).
-        if (req == 0 && kernel == PA_KERNEL_VALU && B % 4 == 0 && part >= kAutoPartitionMin &&
-            part < max_ctx)
+        // µs, one wave -> four, VALU kernel: batch-64 MHA (2048 pairs) 358.7
+        // -> 347.0, at two heads per kv head 373.4 -> 352.4, 256 sequences
+        // 1519 -> 1450, 32 sequences 192.2 -> 186.7; matrix-core kernel: 64
+        // sequences of 16k-32k tokens at 4 heads per kv head (512 pairs) 984
+        // -> 892, 64 sequences at 8 heads per kv head (2048 pairs) 406 -> 366,
+        // gqa_70b (1024 pairs) 188.1 -> 189.2.  Fewer pairs make too few,
+        // too long items to balance: 32 gqa_70b sequences (256 pairs) 68.7
+        // -> 78.7, and 16 long contexts sharing a 4096-token prefix (128
+        // pairs) 226.3 -> 232.8.  A partition halved for a small batch stays
+        // on one wave (8 sequences of up to 2048 tokens: 27.3 against
+        // 29.4-31.8 on four).
+        if (req == 0 && multi_wave_items(kernel, G, B) && (long long)S * Hkv >= kMultiWavePairs &&
+            part >= kAutoPartitionMin && part < max_ctx) {
             part *= 4;
+            multi = true;
+        }
         if (part >= max_ctx) {   // single pass: one partition covers any context
             part = ((max_ctx > 0 ? max_ctx : 1) + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;
         }
@@ -206,13 +227,16 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
     if (kernel == PA_KERNEL_GENERIC) {
         // one pass over the whole context; no workspace.  Grid (Hq, S) of
         // 64-thread work-groups: within the limits for every valid shape.
+        if (req_tw > 1) return PA_ERR_UNSUPPORTED;   // an automatic kernel fell back
         p.kernel = kernel;
         p.partition_tokens = (int)(max_ctx > 0 ? max_ctx : 1);
         p.max_partitions = 1;
         p.split = 0;
-    } else if (decode_grid_mode(S, Hkv, p.max_partitions,
-                                decode_threads(kernel, Hq / Hkv, p.partition_tokens, B)) < 0) {
-        return PA_ERR_SHAPE;
+        p.token_waves = 1;
+    } else {
+        p.token_waves = req_tw > 0 ? req_tw : multi ? waves_for_length(p.partition_tokens) : 1;
+        if (decode_grid_mode(S, Hkv, p.max_partitions, decode_threads(kernel, G, p.token_waves)) < 0)
+            return PA_ERR_SHAPE;
     }
     if (p.split) {
         const size_t rows = (size_t)S * Hq * p.max_partitions;
@@ -273,6 +297,7 @@ pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB,
     const int req = cfg ? cfg->partition_tokens : 0;
     if (req < 0 || (req > 0 && req % pa::kTileTokens != 0)) return PA_ERR_SHAPE;
     if (cfg && (cfg->stages < 0 || cfg->stages > PA_STAGE_ALL)) return PA_ERR_SHAPE;
+    if (cfg && cfg->token_waves != 0 && cfg->token_waves != 1) return PA_ERR_UNSUPPORTED;
     switch (kernel) {
     case PA_KERNEL_AUTO:
         kernel = supports_prefill_mfma(Hq, Hkv, D, B, dtype) ? PA_KERNEL_MFMA : PA_KERNEL_GENERIC;
@@ -287,6 +312,7 @@ pa_status make_prefill_plan(int S, int T, int Hq, int Hkv, int D, int B, int NB,
     }
     const long long max_ctx = (long long)max_blocks * B;
     pa_plan p{};
+    p.token_waves = 1;
     *q_blocks = 0;
     if (kernel == PA_KERNEL_MFMA) {
         const int cols = prefill_columns(Hq / Hkv, max_query_len);
@@ -412,11 +438,10 @@ pa_status pa_decode_ex(const void *query, const void *key_cache, const void *val
     // live-item grid when every work-group can decode its item from the
     // lengths held in one wave's registers and the 1-D grid fits (the plan
     // has checked that one of the two grids fits)
-    a.valu_waves = plan.kernel == PA_KERNEL_VALU ? valu_waves(plan.partition_tokens, B) : 1;
+    a.token_waves = plan.token_waves;
     a.compact = plan.kernel != PA_KERNEL_GENERIC &&
                 decode_grid_mode(S, Hkv, plan.max_partitions,
-                                 decode_threads(plan.kernel, Hq / Hkv, plan.partition_tokens,
-                                                B)) == 1;
+                                 decode_threads(plan.kernel, Hq / Hkv, plan.token_waves)) == 1;
     if (plan.split) {
         const size_t rows = (size_t)S * Hq * plan.max_partitions;
         char *ws = static_cast<char *>(workspace);

@@ -27,7 +27,8 @@ struct Args {
     int split;                // 1: write partials, 0: write final output
     int stream_kv;            // 1: K / V loads carry the non-temporal hint
     int compact;              // 1: 1-D grid decoded into live items (pa_sched.h)
-    int valu_waves;           // waves per item of the VALU kernel (1, 2 or 4)
+    int token_waves;          // waves sharing an item's tokens (1, 2 or 4): the VALU
+                              // kernel and the matrix-core kernel's one-wave groups
     // Multi-token (causal) calls only; query_start is null for decode.
     const int32_t *query_start;   // [S+1] rows query_start[s] .. query_start[s+1]-1 are sequence s's
     int T;                        // query rows; query / out are [T][Hq][D]

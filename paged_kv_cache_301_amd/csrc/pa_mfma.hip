@@ -41,10 +41,15 @@ using namespace mfma;
 constexpr int sub_tiles(int W) { return W == 4 ? 2 : W; }
 constexpr int waves_per_simd(int W) { return W == 4 ? 3 : 2; }
 
-template <typename T, typename OutT, int G, bool SCALAR, bool STREAM>
-__global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)) void mfma_kernel(Args a) {
+// TW token-waves (groups of at most 16 heads, one head wave): wave t runs
+// the item's sub-tiles t, t + TW, ... in an LDS image of its own, with no
+// barrier between the waves until their softmax states meet in LDS at the
+// end (1, 2 or 4, as the plan decides for the VALU kernel too).
+template <typename T, typename OutT, int G, int TW, bool SCALAR, bool STREAM>
+__global__ __launch_bounds__(64 * ((G + 15) / 16) * TW, waves_per_simd((G + 15) / 16)) void mfma_kernel(Args a) {
     using Vec = typename Mfma<T>::Vec;
-    constexpr int W = (G + 15) / 16;          // waves per work-group
+    constexpr int W = (G + 15) / 16;          // head waves per work-group
+    static_assert(W == 1 || TW == 1, "token-waves only for groups of at most 16 heads");
     constexpr int NS = sub_tiles(W);          // 32-token sub-tiles per iteration
     constexpr int KL = kTileLoads * NS / W;   // load instructions per operand per wave
     static_assert(KL * W == kTileLoads * NS && KL <= kTileLoads, "whole row quads per wave");
@@ -66,7 +71,9 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)
         p = blockIdx.y;
     }
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = TW > 1 ? 0 : wv;            // head wave
+    const int wt = TW > 1 ? wv : 0;           // token-wave
     const int i = lane & 15;
     const int g = lane >> 4;
 
@@ -76,8 +83,8 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)
     const int t_end = min(L, t_begin + a.part_tokens);
     const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
 
-    __shared__ uint4 klds[NS][32 * 16];
-    __shared__ uint4 vlds[NS][32 * 16];
+    __shared__ uint4 klds[NS * TW][32 * 16];
+    __shared__ uint4 vlds[NS * TW][32 * 16];
     __shared__ int32_t tbl[SCALAR ? 1 : kTableLds];
 
     // Q^T fragments of this wave's heads; columns past the group are zero
@@ -113,36 +120,46 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)
         ctx.tv.j0 = t_begin >> a.log2B;
         ctx.tbl = tbl;
         if constexpr (!SCALAR) {
-            stage_table<64 * W>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
+            stage_table<64 * W * TW>(tbl, ctx.tv, t_begin, t_end, threadIdx.x);
             __syncthreads();
         }
 
-        constexpr int kIter = 32 * NS;         // tokens per iteration
-        const int niter = (t_end - t_begin + kIter - 1) / kIter;
+        // iterations of this wave: tokens base + kIter it .. + kIter - 1
+        constexpr int kIter = 32 * NS * TW;    // tokens between a wave's iterations
+        const int base = t_begin + 32 * NS * wt;
+        const int niter = TW == 1 || base < t_end ? (t_end - base + kIter - 1) / kIter : 0;
         // this wave's rows: quads KL w .. KL w + KL - 1 of the iteration, i.e.
         // quads k0 .. k0 + KL - 1 of sub-tile u
         const int u = KL * w / kTileLoads;
         const int k0 = KL * w % kTileLoads;
-        const int tw = t_begin + 32 * u;       // this wave's sub-tile of iteration 0
+        const int tw = base + 32 * u;          // this wave's sub-tile of iteration 0
+        // the wave's LDS images (its own when there are several token-waves)
+        uint4 (*const kimg)[32 * 16] = klds + NS * wt;
+        uint4 (*const vimg)[32 * 16] = vlds + NS * wt;
         // One sub-tile of registers: as soon as this wave's sub-tile is in
         // LDS its registers take the loads of the next one, which stay in
         // flight through the barrier and both products.  (Holding two
         // register tiles and prefetching before the compute needs 223 VGPRs
         // instead of 184 and was 1-4 % slower.)  The scheduling barriers keep
         // the compiler from sinking that prefetch below the products.
+        // Several token-waves share no image, and one wave's LDS accesses
+        // are served in order, so they need no barrier inside the loop.
+        auto sync = [] {
+            if constexpr (TW == 1) __syncthreads();
+        };
         KVTileN<KL> tile;
         if constexpr (SCALAR) {
             ctx.load(tile, tw, k0);
             for (int it = 0; it < niter; ++it) {
-                const int t0 = t_begin + kIter * it;
-                mfma_stage(tile, klds[u], vlds[u], g, i, k0);
+                const int t0 = base + kIter * it;
+                mfma_stage(tile, kimg[u], vimg[u], g, i, k0);
                 __builtin_amdgcn_sched_barrier(0);
                 if (it + 1 < niter) ctx.load(tile, tw + kIter * (it + 1), k0);   // uniform
                 __builtin_amdgcn_sched_barrier(0);
-                __syncthreads();   // every wave's rows visible
+                sync();   // every wave's rows visible
                 const int nsub = min(NS, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-                mfma_tiles<T, NS>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
-                __syncthreads();   // reads done before the next stage overwrites LDS
+                mfma_tiles<T, NS>(st, qf, kimg, vimg, t0, nsub, t_end, g, i, sc);
+                sync();   // reads done before the next stage overwrites LDS
             }
         } else {
             // table in LDS (blocks of fewer than 4 tokens, one per row): the
@@ -153,17 +170,46 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)
             ctx.load_ids(tile, ids, tw, k0);
             ctx.ids(ids, tw + kIter, k0);
             for (int it = 0; it < niter; ++it) {
-                const int t0 = t_begin + kIter * it;
-                mfma_stage(tile, klds[u], vlds[u], g, i, k0);
+                const int t0 = base + kIter * it;
+                mfma_stage(tile, kimg[u], vimg[u], g, i, k0);
                 __builtin_amdgcn_sched_barrier(0);
                 if (it + 1 < niter) ctx.load_ids(tile, ids, tw + kIter * (it + 1), k0);   // uniform
                 __builtin_amdgcn_sched_barrier(0);
                 ctx.ids(ids, tw + kIter * (it + 2), k0);
-                __syncthreads();   // every wave's rows visible
+                sync();   // every wave's rows visible
                 const int nsub = min(NS, (t_end - t0 + 31) >> 5);   // >= 1: t0 < t_end
-                mfma_tiles<T, NS>(st, qf, klds, vlds, t0, nsub, t_end, g, i, sc);
-                __syncthreads();   // reads done before the next stage overwrites LDS
+                mfma_tiles<T, NS>(st, qf, kimg, vimg, t0, nsub, t_end, g, i, sc);
+                sync();   // reads done before the next stage overwrites LDS
             }
+        }
+        if constexpr (TW == 1) {
+            st.l += shfl_xor(st.l, 16);
+            st.l += shfl_xor(st.l, 32);
+        }
+    }
+
+    if constexpr (TW > 1) {
+        // token-waves 1 .. TW - 1 leave their states in their own images
+        // (o in the K image, m and l in the V image), wave 0 merges them
+        if (wt > 0) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                klds[wt][64 * n + lane] = bitcast<uint4>(st.o[n]);
+            vlds[wt][lane] = make_uint4(__float_as_uint(st.m), __float_as_uint(st.l), 0u, 0u);
+        }
+        __syncthreads();
+        if (wt > 0) return;
+#pragma unroll
+        for (int v = 1; v < TW; ++v) {
+            const uint4 ml = vlds[v][lane];
+            const float m2 = __uint_as_float(ml.x), l2 = __uint_as_float(ml.y);
+            const float mn = fmaxf(st.m, m2);
+            const float ms = mn == kNegInf ? 0.f : mn;   // neither wave saw a token
+            const float ca = fast_exp2(st.m - ms), cb = fast_exp2(m2 - ms);
+            st.l = st.l * ca + l2 * cb;
+#pragma unroll
+            for (int n = 0; n < 8; ++n) st.o[n] = st.o[n] * ca + bitcast<f32x4>(klds[v][64 * n + lane]) * cb;
+            st.m = mn;
         }
         st.l += shfl_xor(st.l, 16);
         st.l += shfl_xor(st.l, 32);
@@ -193,21 +239,34 @@ __global__ __launch_bounds__(64 * ((G + 15) / 16), waves_per_simd((G + 15) / 16)
     }
 }
 
-template <typename T, typename OutT, int G, bool STREAM>
+template <typename T, typename OutT, int G, int TW, bool STREAM>
 void launch_gs(const Args &a, hipStream_t st) {
     const dim3 grid = a.compact ? dim3((unsigned)((long long)a.Hkv * a.S * a.max_parts))
                                 : dim3(a.Hkv * a.S, a.max_parts);
-    const dim3 block(64 * ((G + 15) / 16));
+    const dim3 block(64 * ((G + 15) / 16) * TW);
     if (a.B % 4 == 0)
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, true, STREAM>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, TW, true, STREAM>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, false, STREAM>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((mfma_kernel<T, OutT, G, TW, false, STREAM>), grid, block, 0, st, a);
+}
+
+template <typename T, typename OutT, int G, int TW>
+void launch_gt(const Args &a, hipStream_t st) {
+    if (a.stream_kv) launch_gs<T, OutT, G, TW, true>(a, st);
+    else launch_gs<T, OutT, G, TW, false>(a, st);
 }
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    if (a.stream_kv) launch_gs<T, OutT, G, true>(a, st);
-    else launch_gs<T, OutT, G, false>(a, st);
+    if constexpr (G <= 16) {
+        switch (a.token_waves) {
+        case 4: launch_gt<T, OutT, G, 4>(a, st); break;
+        case 2: launch_gt<T, OutT, G, 2>(a, st); break;
+        default: launch_gt<T, OutT, G, 1>(a, st); break;
+        }
+    } else {
+        launch_gt<T, OutT, G, 1>(a, st);
+    }
     return hipGetLastError();
 }
 

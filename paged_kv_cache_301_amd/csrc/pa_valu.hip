@@ -99,7 +99,7 @@ __device__ __forceinline__ void valu_compute(ValuState<T, G> &st, const KVTile &
     }
 }
 
-// NW waves per item (1, 2 or 4 by the partition's length): wave w runs the
+// NW waves per item (1, 2 or 4, as the plan decides): wave w runs the
 // item's 32-token tiles w, w + NW, ..., and the waves' softmax states meet
 // in LDS at the end.  Long partitions on several waves need a quarter of the
 // partial results of short ones on one, or none when a partition covers the
@@ -282,8 +282,8 @@ void launch_gw(const Args &a, hipStream_t st) {
 
 template <typename T, typename OutT, int G>
 hipError_t launch_g(const Args &a, hipStream_t st) {
-    if (a.valu_waves == 4) launch_gw<T, OutT, G, 4>(a, st);
-    else if (a.valu_waves == 2) launch_gw<T, OutT, G, 2>(a, st);
+    if (a.token_waves == 4) launch_gw<T, OutT, G, 4>(a, st);
+    else if (a.token_waves == 2) launch_gw<T, OutT, G, 2>(a, st);
     else launch_gw<T, OutT, G, 1>(a, st);
     return hipGetLastError();
 }

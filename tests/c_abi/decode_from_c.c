@@ -142,7 +142,7 @@ static int checked_mode(void *dq, void *dk, void *dv, void *dt, void *dl, void *
 
     /* the environment off, pa_config.check = 1: a length past the table */
     unsetenv("PA_CHECK");
-    const pa_config on = {PA_KERNEL_AUTO, 0, 0, 0, 1};
+    const pa_config on = {PA_KERNEL_AUTO, 0, 0, 0, 1, 0};
     HIP_OK(hipMemset(dout, 0xff, sizeof(float) * S * HQ * D));
     st = pa_decode_ex(dq, dk, dv, dt, dl_bad, scale, dout, S, HQ, HKV, D, B, NB, MAX_BLOCKS,
                       PA_BF16, PA_F32, &on, ws, plan.workspace_bytes, NULL);
@@ -155,7 +155,7 @@ static int checked_mode(void *dq, void *dk, void *dv, void *dt, void *dl, void *
 
     /* PA_CHECK=1 but pa_config.check = -1: unchecked, good inputs */
     setenv("PA_CHECK", "1", 1);
-    const pa_config off = {PA_KERNEL_AUTO, 0, 0, 0, -1};
+    const pa_config off = {PA_KERNEL_AUTO, 0, 0, 0, -1, 0};
     st = pa_decode_ex(dq, dk, dv, dt, dl, scale, dout, S, HQ, HKV, D, B, NB, MAX_BLOCKS,
                       PA_BF16, PA_F32, &off, ws, plan.workspace_bytes, NULL);
     HIP_OK(hipDeviceSynchronize());
@@ -240,7 +240,7 @@ int main(void) {
     };
     int failed = 0;
     for (size_t c = 0; c < sizeof(cases) / sizeof(cases[0]); ++c) {
-        const pa_config cfg = {cases[c].kernel, cases[c].part, 0, 0, 0};
+        const pa_config cfg = {cases[c].kernel, cases[c].part, 0, 0, 0, 0};
         pa_plan plan;
         pa_status st = pa_decode_plan(S, HQ, HKV, D, B, NB, MAX_BLOCKS, PA_BF16, PA_F32, &cfg, &plan);
         if (st != PA_OK) {

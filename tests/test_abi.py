@@ -64,6 +64,18 @@ def test_validation_errors(lib):
     assert _call(lib, cfg=b.PaConfig(9, 0, 0)) == b.PA_ERR_UNSUPPORTED
     # partition not a multiple of 32
     assert _call(lib, cfg=b.PaConfig(b.KERNEL_AUTO, 48, 0)) == b.PA_ERR_SHAPE
+    # token-waves: 0, 1, 2 or 4, above 1 only where the kernel runs them
+    for tw in (3, -1, 8):
+        assert _call(lib, cfg=b.PaConfig(b.KERNEL_AUTO, 0, 0, 0, 0, tw)) == b.PA_ERR_SHAPE
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_GENERIC, 0, 0, 0, 0, 2)) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_AUTO, 0, 0, 0, 0, 2), D=64) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_VALU, 0, 0, 0, 0, 4), B=2) == b.PA_ERR_UNSUPPORTED
+    assert _call(lib, cfg=b.PaConfig(b.KERNEL_MFMA, 0, 0, 0, 0, 2), Hq=64, Hkv=2) == \
+        b.PA_ERR_UNSUPPORTED
+    p = b.PaPlan()
+    assert lib.pa_prefill_plan(2, 8, 4, 2, 128, 16, 8, 4, 4, BF16, BF16,
+                               ctypes.byref(b.PaConfig(b.KERNEL_AUTO, 0, 0, 0, 0, 2)),
+                               ctypes.byref(p)) == b.PA_ERR_UNSUPPORTED
 
 
 def test_empty_batch_is_noop(lib):
@@ -76,14 +88,32 @@ def test_plans():
     # here the whole context (one pass, no workspace)
     p = b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16)
     assert p["kernel"] == b.KERNEL_VALU and p["split"] == 0 and p["partition_tokens"] == 4096
-    assert p["workspace_bytes"] == 0
+    assert p["workspace_bytes"] == 0 and p["token_waves"] == 4
     p = b.plan(64, 32, 32, 128, 16, 15360, 1024, torch.bfloat16)     # 16k-token tables
     assert p["split"] == 1 and p["partition_tokens"] == 4096 and p["max_partitions"] == 4
     assert p["workspace_bytes"] >= 64 * 32 * p["max_partitions"] * (128 + 2) * 4
-    # a partition halved for a small batch, or one-token blocks, stay on one wave
-    assert b.plan(8, 32, 32, 128, 16, 15360, 128, torch.bfloat16)["partition_tokens"] == 128
+    assert p["token_waves"] == 4
+    # a partition halved for a small batch, one-token blocks, or a batch of
+    # fewer than 512 (sequence, kv head) pairs stay on one wave
+    p = b.plan(8, 32, 32, 128, 16, 15360, 128, torch.bfloat16)
+    assert p["partition_tokens"] == 128 and p["token_waves"] == 1
     p = b.plan(64, 32, 32, 128, 1, 300000, 4096, torch.bfloat16)
-    assert p["partition_tokens"] <= 1024
+    assert p["partition_tokens"] <= 1024 and p["token_waves"] == 1
+    p = b.plan(16, 32, 8, 128, 16, 100000, 2048, torch.bfloat16)    # 128 pairs, 32k tokens
+    assert p["kernel"] == b.KERNEL_MFMA and p["partition_tokens"] == 1024
+    assert p["token_waves"] == 1
+    p = b.plan(128, 64, 8, 128, 16, 100000, 512, torch.bfloat16)    # 1024 pairs, 8k tokens
+    assert p["partition_tokens"] == 4096 and p["token_waves"] == 4
+    # a four-fold partition cut to a shorter longest context: waves of at
+    # least about 1024 tokens each
+    p = b.plan(64, 32, 32, 128, 16, 15360, 160, torch.bfloat16)     # 2560 tokens
+    assert p["split"] == 0 and p["token_waves"] == 2
+    # an explicit partition runs on one wave unless more are asked for
+    p = b.plan(64, 32, 32, 128, 16, 15360, 1024, torch.bfloat16, partition_tokens=4096)
+    assert p["token_waves"] == 1
+    p = b.plan(64, 32, 32, 128, 16, 15360, 1024, torch.bfloat16, partition_tokens=4096,
+               token_waves=2)
+    assert p["partition_tokens"] == 4096 and p["token_waves"] == 2
     assert b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16,
                   kernel="mfma")["kernel"] == b.KERNEL_MFMA
     assert b.plan(8, 16, 8, 128, 16, 645, 128, torch.float16)["kernel"] == b.KERNEL_VALU

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-RECORD = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) P=(\d+) "
+RECORD = re.compile(r"traffic-record: kernel=(\S+) workload=(\S+) B=(\d+) P=(\d+) TW=(\d+) "
                     r"source_sha256=([0-9a-f]+) read_bytes=(\d+) write_bytes=(\d+)")
 
 
@@ -59,10 +59,10 @@ def test_traffic_records_are_well_formed():
     recs = records()
     assert recs, "no traffic records under profiles/"
     seen = set()
-    for path, kernel, workload, B, P, sha, rb, wb in recs:
+    for path, kernel, workload, B, P, TW, sha, rb, wb in recs:
         assert kernel in bench.KERNEL_SOURCES, (path, kernel)
-        assert int(rb) > 0 and int(wb) >= 0, path
-        key = (kernel, workload, int(B), int(P), sha)
+        assert int(rb) > 0 and int(wb) >= 0 and int(TW) in (1, 2, 4), path
+        key = (kernel, workload, int(B), int(P), int(TW), sha)
         assert key not in seen, f"duplicate record {key} in {path}"
         seen.add(key)
 
@@ -74,18 +74,20 @@ def test_traffic_records_are_well_formed():
 ])
 def test_headline_workloads_have_current_records(kernel, workload, B):
     """The decode workloads the targets name carry HBM traffic measured on the
-    current kernel sources, at the partition the automatic plan picks.  After
+    current kernel sources, at the partition and token-waves the automatic
+    plan picks.  After
     a kernel change the records are stale until the profiles are taken again:
     reported as a skip naming the record (the bench line then reports traffic
     null), not as a failure."""
     from paged_kv_cache_301_amd import binding, workloads
     sp = workloads.SPECS[workload].replace(B=B)
     max_blocks = (sp.max_len + B - 1) // B
-    P = binding.plan(sp.S, sp.Hq, sp.Hkv, sp.D, B, 1 << 20, max_blocks,
-                     workloads._DTYPES[sp.dtype])["partition_tokens"]
-    assert any(r[1:5] == (kernel, workload, str(B), str(P)) for r in records()), \
-        f"no record at all for {kernel} {workload} B={B} P={P}"
-    got = bench.recorded_traffic(kernel, workload, B, P)
+    p = binding.plan(sp.S, sp.Hq, sp.Hkv, sp.D, B, 1 << 20, max_blocks,
+                     workloads._DTYPES[sp.dtype])
+    P, TW = p["partition_tokens"], p["token_waves"]
+    assert any(r[1:6] == (kernel, workload, str(B), str(P), str(TW)) for r in records()), \
+        f"no record at all for {kernel} {workload} B={B} P={P} TW={TW}"
+    got = bench.recorded_traffic(kernel, workload, B, P, TW)
     if got is None:
         pytest.skip(f"traffic record for {kernel} {workload} predates the current kernel "
                     "sources: profile again")

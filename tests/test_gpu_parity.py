@@ -521,30 +521,38 @@ def test_pool_beyond_4gib_small_blocks(kernel, Hq, Hkv, B):
     torch.cuda.empty_cache()
 
 
-# ------------------------------------------- VALU kernel: waves per item
+# ------------------------------------------------- token-waves per item
 
-@pytest.mark.parametrize("Hq,Hkv,B,part", [(8, 8, 16, 2048), (8, 8, 16, 4096), (16, 8, 4, 4096),
-                                           (8, 8, 16, 8192), (16, 8, 16, 2048), (8, 8, 32, 4096)])
-def test_valu_waves_per_item(Hq, Hkv, B, part):
-    """Partitions of 2048 (4096 and more) tokens run on two (four) waves of
-    one work-group, each streaming every second (fourth) 32-token tile, their
-    softmax states merged in LDS; a partition covering the context is one
-    pass.  Every row against the oracle, the workspace NaN-filled, with
+@pytest.mark.parametrize("kernel,Hq,Hkv,B,part,tw", [
+    ("valu", 8, 8, 16, 2048, 2), ("valu", 8, 8, 16, 4096, 4), ("valu", 16, 8, 4, 4096, 4),
+    ("valu", 8, 8, 16, 8192, 4), ("valu", 16, 8, 16, 2048, 2), ("valu", 8, 8, 32, 4096, 4),
+    ("valu", 8, 8, 16, 1024, 4),
+    ("mfma", 32, 8, 16, 2048, 2), ("mfma", 32, 8, 16, 4096, 4), ("mfma", 64, 8, 4, 8192, 4),
+    ("mfma", 128, 8, 16, 4096, 4), ("mfma", 8, 8, 32, 2048, 2), ("mfma", 16, 2, 16, 4096, 4),
+    ("mfma", 32, 8, 16, 512, 4)])
+def test_waves_per_item(kernel, Hq, Hkv, B, part, tw):
+    """Items run on two or four waves of one work-group (pa_config
+    token_waves), each streaming every second or fourth 32-token tile of the
+    partition, their softmax states merged in LDS (the VALU kernel, and the
+    matrix-core kernel's groups of at most 16 heads); a partition covering
+    the context is one pass, and a short one leaves some waves without a
+    tile.  Every row against the oracle, the workspace NaN-filled, with
     empty, one-tile and ragged contexts."""
-    say(f"case: VALU waves per item Hq={Hq} Hkv={Hkv} B={B} part={part}")
+    say(f"case: waves per item {kernel} Hq={Hq} Hkv={Hkv} B={B} part={part} tw={tw}")
     lens = (1, 33, 1000, 4096, 5000, 2047, 0, 8191)
-    spec = workloads.WorkloadSpec("valu_waves", S=len(lens), Hq=Hq, Hkv=Hkv, D=128, B=B,
+    spec = workloads.WorkloadSpec("token_waves", S=len(lens), Hq=Hq, Hkv=Hkv, D=128, B=B,
                                   dtype="bf16", lens=("fixed", lens), max_len=8192,
                                   pool=("free", 0.2), seed=700 + part // 1024 + B)
     w = workloads.make_workload(spec, device=DEV, poison=True)
-    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, kernel="valu",
-                     partition_tokens=part)
-    assert p["kernel"] == binding.KERNEL_VALU and p["partition_tokens"] == part
+    kw = dict(kernel=kernel, partition_tokens=part, token_waves=tw)
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, **kw)
+    assert p["kernel"] == binding.KERNELS[kernel] and p["partition_tokens"] == part
+    assert p["token_waves"] == tw
     ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
           if p["workspace_bytes"] else None)
     ref = oracle_full(w)
-    out = run(w, out_dtype=torch.float32, kernel="valu", partition_tokens=part, workspace=ws)
-    check(out, ref, torch.bfloat16, f"valu waves part={part}")
+    out = run(w, out_dtype=torch.float32, workspace=ws, **kw)
+    check(out, ref, torch.bfloat16, f"{kernel} waves part={part} tw={tw}")
     assert torch.equal(out[6], torch.zeros_like(out[6]))
-    check(run(w, kernel="valu", partition_tokens=part, workspace=ws), ref, torch.bfloat16,
-          f"valu waves part={part}/native")
+    check(run(w, workspace=ws, **kw), ref, torch.bfloat16,
+          f"{kernel} waves part={part} tw={tw}/native")

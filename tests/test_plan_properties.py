@@ -14,7 +14,11 @@ planner accepts must satisfy what the kernels assume of it:
   work-groups by the longest chunk);
 * a split plan's workspace holds every partial result (o, m, l in fp32);
 * an explicit partition is honoured unless it is not needed (one pass),
-  too small for the grid or too large for the table slice.
+  too small for the grid or too large for the table slice;
+* items run on 1, 2 or 4 token-waves: the count asked for, else more than
+  one only where the planner made the partition four times as long (at
+  least 512 (sequence, kv head) pairs, about 1024 tokens or more per wave),
+  and only on the kernels that run them.
 
 and everything it refuses carries the documented status."""
 import ctypes
@@ -76,13 +80,14 @@ shapes = st.fixed_dictionaries({
     "kernel": st.sampled_from(sorted(KERNELS)),
     "part": st.one_of(st.just(0), st.integers(1, 200).map(lambda k: TILE * k),
                       st.integers(1, 1 << 16)),
+    "tw": st.sampled_from([0, 0, 0, 1, 2, 4, 3]),
 })
 
 
 def decode_plan(sh):
     Hq = sh["G"] * sh["Hkv"]
     odt = b.PA_F32 if sh["odt_f32"] else sh["dt"]
-    cfg = b.PaConfig(KERNELS[sh["kernel"]], sh["part"], 0, 0, 0)
+    cfg = b.PaConfig(KERNELS[sh["kernel"]], sh["part"], 0, 0, 0, sh["tw"])
     p = b.PaPlan()
     st_ = b.load().pa_decode_plan(sh["S"], Hq, sh["Hkv"], sh["D"], sh["B"], sh["NB"],
                                   sh["max_blocks"], sh["dt"], odt, ctypes.byref(cfg),
@@ -105,7 +110,7 @@ def test_decode_plan_properties(sh):
     if D > 512:
         assert st_ == b.PA_ERR_UNSUPPORTED
         return
-    if req % TILE != 0:
+    if req % TILE != 0 or sh["tw"] not in (0, 1, 2, 4):
         assert st_ == b.PA_ERR_SHAPE
         return
     if forced in (b.KERNEL_VALU, b.KERNEL_MFMA) and not supports(forced, Hq, Hkv, D, B, dt):
@@ -120,6 +125,16 @@ def test_decode_plan_properties(sh):
     assert p.kernel in (b.KERNEL_GENERIC, b.KERNEL_VALU, b.KERNEL_MFMA)
     assert forced == b.KERNEL_AUTO or p.kernel == forced
     assert supports(p.kernel, Hq, Hkv, D, B, dt)
+    G = Hq // Hkv
+    multi_ok = B % 4 == 0 and (p.kernel == b.KERNEL_VALU or (p.kernel == b.KERNEL_MFMA and G <= 16))
+    assert sh["tw"] <= 1 or multi_ok
+    if sh["tw"]:
+        assert p.token_waves == sh["tw"]
+    else:
+        assert p.token_waves in (1, 2, 4)
+        if p.token_waves > 1:
+            assert multi_ok and req == 0 and S * Hkv >= 512
+            assert p.partition_tokens >= 1024 * p.token_waves
     if p.kernel == b.KERNEL_GENERIC:
         assert p.split == 0 and p.workspace_bytes == 0 and p.max_partitions == 1
         assert p.partition_tokens >= max(max_ctx, 1)
@@ -132,9 +147,9 @@ def test_decode_plan_properties(sh):
     if B % 4 != 0:
         assert ceil_div(P, B) <= TABLE_LDS
     if p.kernel == b.KERNEL_MFMA:
-        threads = 64 * ceil_div(Hq // Hkv, 16)
-    else:   # VALU: 1, 2 or 4 waves per item by the partition's length
-        threads = 64 * (1 if B % 4 else 4 if P >= 4096 else 2 if P >= 2048 else 1)
+        threads = 64 * ceil_div(G, 16) * p.token_waves
+    else:
+        threads = 64 * p.token_waves
     compact = S <= SCHED_MAX_SEQS and S * Hkv * parts * threads < LAUNCH_LIMIT
     rect = S * Hkv * threads < LAUNCH_LIMIT and parts <= MAX_PARTS
     assert compact or rect
@@ -149,7 +164,7 @@ def test_decode_plan_properties(sh):
         too_big = cap is not None and req > cap
         if not (single or too_small or too_big):
             assert P == req
-    if forced == b.KERNEL_AUTO and req == 0 and sh["odt_f32"] is False:
+    if forced == b.KERNEL_AUTO and req == 0 and sh["tw"] == 0 and sh["odt_f32"] is False:
         # the automatic plan is what pa_decode_workspace_bytes reports
         n = b.load().pa_decode_workspace_bytes(S, Hq, Hkv, D, B, sh["NB"], sh["max_blocks"],
                                                dt, dt)
