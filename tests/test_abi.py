@@ -185,6 +185,24 @@ def test_environment_overrides(monkeypatch):
         b.plan(*args)
 
 
+def test_token_waves_override(monkeypatch):
+    '''PA_TOKEN_WAVES fills in the decode waves per item a call leaves to the
+    library; an explicit token_waves wins, and the multi-token planner never
+    reads it.'''
+    args = (64, 32, 8, 128, 16, 15360, 1024, torch.bfloat16)      # 512 pairs, 16k tables
+    assert b.plan(*args)["token_waves"] == 4
+    monkeypatch.setenv("PA_TOKEN_WAVES", "1")
+    assert b.plan(*args)["token_waves"] == 1
+    assert b.plan(*args, token_waves=2)["token_waves"] == 2
+    monkeypatch.setenv("PA_TOKEN_WAVES", "2")
+    assert b.plan(*args, partition_tokens=1024)["token_waves"] == 2
+    p = b.plan_prefill(4, 64, 32, 8, 128, 16, 15360, 256, 16, torch.bfloat16)
+    assert p["token_waves"] == 1
+    monkeypatch.setenv("PA_TOKEN_WAVES", "3")
+    with pytest.raises(b.PaError):
+        b.plan(*args)
+
+
 def test_read_bytes_validation(lib):
     fake = 1 << 20
     assert lib.pa_read_bytes(None, 0, None, None) == b.PA_OK
