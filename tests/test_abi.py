@@ -100,8 +100,14 @@ def test_plans():
     p = b.plan(64, 32, 32, 128, 1, 300000, 4096, torch.bfloat16)
     assert p["partition_tokens"] <= 1024 and p["token_waves"] == 1
     p = b.plan(16, 32, 8, 128, 16, 100000, 2048, torch.bfloat16)    # 128 pairs, 32k tokens
-    assert p["kernel"] == b.KERNEL_MFMA and p["partition_tokens"] == 1024
-    assert p["token_waves"] == 1
+    assert p["kernel"] == b.KERNEL_MFMA and p["token_waves"] == 1
+    # ... whose one-wave items would exceed a round of resident waves by a
+    # third at 1024 tokens: 2048 (one round at the table width)
+    assert p["partition_tokens"] == 2048
+    # with one-token blocks the LDS table slice caps it at 1024
+    assert b.plan(16, 32, 8, 128, 1, 100000, 32768, torch.bfloat16)["partition_tokens"] == 1024
+    # short contexts in a small batch keep the halving to two rounds
+    assert b.plan(32, 64, 8, 128, 16, 100000, 512, torch.bfloat16)["partition_tokens"] == 512
     p = b.plan(128, 64, 8, 128, 16, 100000, 512, torch.bfloat16)    # 1024 pairs, 8k tokens
     assert p["partition_tokens"] == 4096 and p["token_waves"] == 4
     # a four-fold partition cut to a shorter longest context: waves of at
