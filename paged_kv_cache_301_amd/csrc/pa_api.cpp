@@ -43,22 +43,22 @@ long long resident_waves(int waves) { return waves == 4 ? 3072 : kResidentWaves;
 // Wide groups (several waves per work-group) have few resident work-groups
 // and large partial results, so their partition also doubles while the
 // items, counted at the full table width, would exceed a round of resident
-// waves by more than a third (batches rarely fill their tables).  So do
-// one-wave items in batches below kMultiWavePairs (sequence, kv head) pairs,
-// which get no token-waves, when their contexts are long enough to exceed
-// that at the base partition; the small-batch halving then does not apply.
-// 16 contexts of 16k-32k tokens at 4 heads per kv head (128 pairs) take
-// 2048-token partitions, about 1500 items in one round, instead of about
-// 3000 in 1.47 rounds at 1024: cold step 221.3 / 222.1 -> 213.8 / 213.2 us
-// (B = 16), 224.8 / 225.2 -> 217.5 / 219.6 (B = 8), 219.1 / 219.8 -> 212.7
-// / 214.8 (B = 32), A/B on one box.  Batches that fill a round only at the
-// table width keep the halving to two: their tables are mostly empty
-// (one round at the table width was slower on 8 sequences of up to 2048 or
-// 4096 tokens, 28.2 -> 29.4 and 57.9 -> 61.2 us, and on 32 of 128 - 8192,
-// 69.8 -> 71.9).  On the
+// waves by more than a third (batches rarely fill their tables).  On the
 // 256-sequence multi-query workload this keeps 1024 tokens at 64 heads
 // (cold step 83.0 / 84.6 us against 88.3 / 89.4 at 2048; 1280 gave 80.7 /
 // 83.2, 768 87.1 / 88.5) and at 32 heads (3993 vs 3643 GB/s at 1536).
+// One-wave items in batches below kMultiWavePairs (sequence, kv head)
+// pairs, which get no token-waves, double the same way when their contexts
+// are long enough to exceed that at the base partition, and the small-batch
+// halving then does not apply.  16 contexts of 16k-32k tokens at 4 heads per
+// kv head (128 pairs) take 2048-token partitions, about 1500 items in one
+// round, instead of about 3000 in 1.47 rounds at 1024: cold step 221.3 /
+// 222.1 -> 213.8 / 213.2 us (B = 16), 224.8 / 225.2 -> 217.5 / 219.6
+// (B = 8), 219.1 / 219.8 -> 212.7 / 214.8 (B = 32), A/B on one box.
+// Batches that fill a round only at the table width keep the halving to
+// two rounds: their tables are mostly empty (one round at the table width
+// was slower on 8 sequences of up to 2048 or 4096 tokens, 28.2 -> 29.4 and
+// 57.9 -> 61.2 us, and on 32 of 128 - 8192, 69.8 -> 71.9).
 long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
     if (max_ctx <= kAutoSinglePass) return max_ctx;
     long long part = kAutoPartitionMin;
