@@ -9,11 +9,14 @@
 // columns per wave.  One work-group handles one (sequence, kv head, context
 // partition) with W = ceil(G / 16) waves: wave w owns query heads 16 w .. 16 w
 // + 15 of the group (G = Hq with one kv head is multi-query attention).  An
-// iteration covers 32 W tokens: wave u loads the 32-token sub-tile u (two
-// 16-row score tiles, one 32-deep P.V step) and stages it in LDS; then every
-// wave runs the contractions for its own heads over all W sub-tiles, so each
-// K / V byte is read from HBM once for all G heads and each wave keeps a whole
-// sub-tile of loads in flight, as in the one-wave case.
+// iteration covers NS 32-token sub-tiles (two 16-row score tiles and one
+// 32-deep P.V step each; NS = W, except two for four waves): the waves load
+// the sub-tiles' rows between them (one sub-tile each, or half of one at
+// four waves) and stage them in LDS, then every wave runs the contractions
+// for its own heads over all NS sub-tiles, so each K / V byte is read from
+// HBM once for all G heads.  Groups of at most 16 heads (one head wave) can
+// also run an item on 2 or 4 token-waves, each streaming its own share of
+// the sub-tiles, their softmax states merged in LDS at the end.
 //
 // The lane layout of both products, the LDS staging and the two-term
 // probability split are in pa_mfma_core.h.
