@@ -556,3 +556,50 @@ def test_waves_per_item(kernel, Hq, Hkv, B, part, tw):
     assert torch.equal(out[6], torch.zeros_like(out[6]))
     check(run(w, workspace=ws, **kw), ref, torch.bfloat16,
           f"{kernel} waves part={part} tw={tw}/native")
+
+
+def _wave_sweep_case(i):
+    """A seeded random shape for the token-wave sweep: kernel family, group,
+    kv heads, block size, type, waves, partition and a ragged length mix
+    with empty, one-token and partition-multiple contexts."""
+    rng = np.random.default_rng(9100 + i)
+    kernel = ("valu", "mfma")[i % 2]
+    G = int(rng.choice((1, 2, 4, 8) if kernel == "valu" else (1, 2, 4, 8, 16)))
+    Hkv = int(rng.choice((1, 2, 4)))
+    B = int(rng.choice((4, 8, 16, 32, 64)))
+    dtype = ("bf16", "f16")[(i // 2) % 2]
+    tw = int(rng.choice((2, 4)))
+    part = 32 * int(rng.integers(1, 65))
+    S = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(0, 3000, size=S)]
+    special = (0, 1, part, 2 * part + 1, 31, 33)
+    for k in range(min(S, 2)):
+        lens[int(rng.integers(0, S))] = int(rng.choice(special))
+    max_len = max(max(lens), 1) + int(rng.integers(0, 2 * B))
+    return kernel, G, Hkv, B, dtype, tw, part, lens, max_len
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_token_wave_sweep(i):
+    """Random shapes through explicit 2- and 4-wave items on both kernel
+    families: every row against the oracle (fp32 output and the native
+    type), empty contexts exactly zero, the workspace NaN-filled."""
+    kernel, G, Hkv, B, dtype, tw, part, lens, max_len = _wave_sweep_case(i)
+    say(f"case: wave sweep {i}: {kernel} G={G} Hkv={Hkv} B={B} {dtype} tw={tw} part={part} "
+        f"lens={lens} max_len={max_len}")
+    spec = workloads.WorkloadSpec("wave_sweep", S=len(lens), Hq=G * Hkv, Hkv=Hkv, D=128, B=B,
+                                  dtype=dtype, lens=("fixed", tuple(lens)), max_len=max_len,
+                                  pool=("free", 0.2), seed=9200 + i)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    kw = dict(kernel=kernel, partition_tokens=part, token_waves=tw)
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, **kw)
+    assert p["token_waves"] == tw
+    ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+          if p["workspace_bytes"] else None)
+    ref = oracle_full(w)
+    out = run(w, out_dtype=torch.float32, workspace=ws, **kw)
+    check(out, ref, DT[dtype], f"wave sweep {i}")
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(out[s], torch.zeros_like(out[s]))
+    check(run(w, workspace=ws, **kw), ref, DT[dtype], f"wave sweep {i}/native")
