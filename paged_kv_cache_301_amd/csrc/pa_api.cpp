@@ -3,6 +3,7 @@
 //
 // Validation and planning are plain host code with no HIP calls, so they run
 // (and are tested) on machines without a GPU.
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <cstdlib>
@@ -35,6 +36,8 @@ constexpr long long kMultiWavePairs = 512;
 // work-group).
 constexpr long long kResidentWaves = 2048;
 long long resident_waves(int waves) { return waves == 4 ? 3072 : kResidentWaves; }
+// Resident waves of the VALU kernel: 3 per SIMD (161 VGPRs).
+constexpr long long kValuResidentWaves = 3072;
 
 // waves: waves per work-group (the matrix-core kernel runs ceil(G / 16)).
 // Measured with the longest-first item order: 1024-token partitions beat 512
@@ -136,10 +139,12 @@ bool multi_wave_items(int kernel, int G, int B) {
     return (kernel == PA_KERNEL_VALU || (kernel == PA_KERNEL_MFMA && G <= 16)) && B % 4 == 0;
 }
 
-// Waves for a partition the planner made multi-wave: about 1024 tokens or
-// more each (a single-pass partition cut to the longest context can be
-// shorter than the four-fold one).
-int waves_for_length(long long part) { return part >= 4096 ? 4 : part >= 2048 ? 2 : 1; }
+// Waves for a partition the planner made multi-wave: at most 1024 tokens
+// each (a single-pass partition cut to the longest context can be shorter
+// than the four-fold one).  Batch-64 MHA with every context 3000 tokens,
+// one pass of 3008: cold step 518.9 / 519.1 us on two waves, 483.3 / 486.4
+// on four.
+int waves_for_length(long long part) { return part > 2048 ? 4 : part > 1024 ? 2 : 1; }
 
 // Threads per work-group of a decode kernel family (the matrix-core kernel
 // runs ceil(G / 16) head waves, times its token-waves).
@@ -217,10 +222,28 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
         // pairs) 226.3 -> 232.8.  A partition halved for a small batch stays
         // on one wave (8 sequences of up to 2048 tokens: 27.3 against
         // 29.4-31.8 on four).
-        if (req == 0 && multi_wave_items(kernel, G, B) && (long long)S * Hkv >= kMultiWavePairs &&
-            part >= kAutoPartitionMin && part < max_ctx) {
-            part *= 4;
-            multi = true;
+        if (req == 0 && multi_wave_items(kernel, G, B) && (long long)S * Hkv >= kMultiWavePairs) {
+            if (part >= kAutoPartitionMin && part < max_ctx) {
+                part *= 4;
+                multi = true;
+            } else if (part < kAutoPartitionMin && max_ctx > kAutoSinglePass) {
+                // halved for a short-context batch: rather one pass (or 4096-token
+                // partitions) on up to four waves, when those still fill a
+                // round of resident waves.  128 sequences at 8 heads per kv
+                // head, every context 1500 tokens: cold step 163.7 / 164.1 us on
+                // 256-token one-wave items, 133.3 / 131.8 in one pass on two
+                // waves; every context 3000: 300.1 / 300.5 on 512-token items,
+                // 256.2 / 255.9 in one pass on four.
+                const long long tw_part = std::min(4 * kAutoPartitionMin, max_ctx);
+                const long long tw_waves = (long long)S * Hkv * ((max_ctx + tw_part - 1) / tw_part) *
+                                           waves_for_length(tw_part);
+                const long long slots =
+                    kernel == PA_KERNEL_VALU ? kValuResidentWaves : resident_waves(1);
+                if (tw_waves >= slots) {
+                    part = tw_part;
+                    multi = true;
+                }
+            }
         }
         if (part >= max_ctx) {   // single pass: one partition covers any context
             part = ((max_ctx > 0 ? max_ctx : 1) + pa::kTileTokens - 1) / pa::kTileTokens * pa::kTileTokens;

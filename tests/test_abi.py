@@ -110,10 +110,18 @@ def test_plans():
     assert b.plan(32, 64, 8, 128, 16, 100000, 512, torch.bfloat16)["partition_tokens"] == 512
     p = b.plan(128, 64, 8, 128, 16, 100000, 512, torch.bfloat16)    # 1024 pairs, 8k tokens
     assert p["partition_tokens"] == 4096 and p["token_waves"] == 4
-    # a four-fold partition cut to a shorter longest context: waves of at
-    # least about 1024 tokens each
+    # a four-fold partition cut to a shorter longest context: enough waves
+    # that each streams at most 1024 tokens
     p = b.plan(64, 32, 32, 128, 16, 15360, 160, torch.bfloat16)     # 2560 tokens
+    assert p["split"] == 0 and p["token_waves"] == 4
+    p = b.plan(64, 32, 32, 128, 16, 15360, 94, torch.bfloat16)      # 1504 tokens
     assert p["split"] == 0 and p["token_waves"] == 2
+    # a short-context batch that would halve its partition below 1024 tokens
+    # runs one pass on waves instead, when those fill a round of slots
+    p = b.plan(128, 64, 8, 128, 16, 15360, 94, torch.bfloat16)      # 1024 pairs, 1504 tokens
+    assert p["kernel"] == b.KERNEL_MFMA and p["split"] == 0 and p["token_waves"] == 2
+    p = b.plan(16, 32, 32, 128, 16, 15360, 256, torch.bfloat16)     # 512 pairs, VALU
+    assert p["partition_tokens"] == 512 and p["token_waves"] == 1   # 2048 waves: too few
     # an explicit partition runs on one wave unless more are asked for
     p = b.plan(64, 32, 32, 128, 16, 15360, 1024, torch.bfloat16, partition_tokens=4096)
     assert p["token_waves"] == 1

@@ -16,8 +16,8 @@ planner accepts must satisfy what the kernels assume of it:
 * an explicit partition is honoured unless it is not needed (one pass),
   too small for the grid or too large for the table slice;
 * items run on 1, 2 or 4 token-waves: the count asked for, else more than
-  one only where the planner made the partition four times as long (at
-  least 512 (sequence, kv head) pairs, about 1024 tokens or more per wave),
+  one only in batches of at least 512 (sequence, kv head) pairs whose
+  partition the planner lengthened for them (more than 512 tokens a wave),
   and only on the kernels that run them.
 
 and everything it refuses carries the documented status."""
@@ -134,7 +134,7 @@ def test_decode_plan_properties(sh):
         assert p.token_waves in (1, 2, 4)
         if p.token_waves > 1:
             assert multi_ok and req == 0 and S * Hkv >= 512
-            assert p.partition_tokens >= 1024 * p.token_waves
+            assert p.partition_tokens > 512 * p.token_waves   # at most 1024 tokens a wave
     if p.kernel == b.KERNEL_GENERIC:
         assert p.split == 0 and p.workspace_bytes == 0 and p.max_partitions == 1
         assert p.partition_tokens >= max(max_ctx, 1)
