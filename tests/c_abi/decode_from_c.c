@@ -233,18 +233,23 @@ int main(void) {
     printf("NULL query -> %s\n", pa_status_string(bad));
     if (bad != PA_ERR_NULL) return 1;
 
-    const struct { int kernel, part; const char *name; } cases[] = {
-        {PA_KERNEL_AUTO, 0, "auto"},       {PA_KERNEL_GENERIC, 0, "generic"},
-        {PA_KERNEL_VALU, 64, "valu/split"}, {PA_KERNEL_MFMA, 0, "mfma"},
-        {PA_KERNEL_MFMA, 96, "mfma/split"},
+    const struct { int kernel, part, waves; const char *name; } cases[] = {
+        {PA_KERNEL_AUTO, 0, 0, "auto"},        {PA_KERNEL_GENERIC, 0, 0, "generic"},
+        {PA_KERNEL_VALU, 64, 0, "valu/split"}, {PA_KERNEL_MFMA, 0, 0, "mfma"},
+        {PA_KERNEL_MFMA, 96, 0, "mfma/split"}, {PA_KERNEL_VALU, 256, 2, "valu/2 waves"},
+        {PA_KERNEL_MFMA, 512, 4, "mfma/4 waves"},
     };
     int failed = 0;
     for (size_t c = 0; c < sizeof(cases) / sizeof(cases[0]); ++c) {
-        const pa_config cfg = {cases[c].kernel, cases[c].part, 0, 0, 0, 0};
+        const pa_config cfg = {cases[c].kernel, cases[c].part, 0, 0, 0, cases[c].waves};
         pa_plan plan;
         pa_status st = pa_decode_plan(S, HQ, HKV, D, B, NB, MAX_BLOCKS, PA_BF16, PA_F32, &cfg, &plan);
         if (st != PA_OK) {
             fprintf(stderr, "%s: plan: %s\n", cases[c].name, pa_status_string(st));
+            return 2;
+        }
+        if (cases[c].waves && plan.token_waves != cases[c].waves) {
+            fprintf(stderr, "%s: plan runs %d waves per item\n", cases[c].name, plan.token_waves);
             return 2;
         }
         void *ws = NULL;
@@ -262,8 +267,9 @@ int main(void) {
         /* |got - ref| <= 2e-3 * max(|ref|, 1e-2 * max over the row |ref|) */
         const double worst = max_rel_err(got, ref);
         const int ok = worst <= 2e-3;
-        printf("%-11s kernel %d partition %5d split %d: max rel err %.3e %s\n", cases[c].name,
-               plan.kernel, plan.partition_tokens, plan.split, worst, ok ? "ok" : "FAIL");
+        printf("%-12s kernel %d partition %5d split %d waves %d: max rel err %.3e %s\n",
+               cases[c].name, plan.kernel, plan.partition_tokens, plan.split, plan.token_waves,
+               worst, ok ? "ok" : "FAIL");
         failed |= !ok;
     }
     failed |= checked_mode(dq, dk, dv, dt, dl, dout, tables, NB, scale, ref, got);

@@ -30,6 +30,7 @@ def test_decode_from_plain_c():
     r = subprocess.run([EXE], capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count(": max rel err") == 5 and "FAIL" not in r.stdout
+    assert r.stdout.count(": max rel err") == 7 and "FAIL" not in r.stdout
+    assert "waves 2:" in r.stdout and "waves 4:" in r.stdout
     # checked mode: rejected before any attention kernel, reported once
     assert r.stdout.count(": ok") == 4
