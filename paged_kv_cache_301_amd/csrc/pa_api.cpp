@@ -578,6 +578,18 @@ pa_status pa_prefill(const void *query, const void *key_cache, const void *value
     a.T = T;
     a.q_blocks = qb;
     a.prefill_columns = prefill_columns(Hq / Hkv, max_query_len);
+    // Longest contexts first when the work-groups take more than one round
+    // of the resident ones (two waves per SIMD: 8 / waves per work-group on
+    // each of 256 CUs); in one round every work-group starts at once and the
+    // order only delays each start by the length lookup.  Chunked-prefill
+    // batch (16 sequences of 1024-8192 tokens, the last 512 new, four rounds):
+    // 611 -> 628-636 TFLOP/s per step, 650-654 -> 686-694 at 8 heads per kv
+    // head; 4 new tokens per sequence (one round): 71 -> 78 us if ordered.
+    {
+        const long long wgs = ((long long)S * Hkv + 7) / 8 * 8 * qb * plan.max_partitions;
+        const long long resident = 256LL * (8 / (2 * a.prefill_columns / 64));
+        a.by_length = plan.kernel == PA_KERNEL_MFMA && S <= pa::kSchedMaxSeqs && wgs > resident;
+    }
     if (plan.split) {
         const size_t rows = (size_t)T * Hq * plan.max_partitions;
         char *ws = static_cast<char *>(workspace);

@@ -34,6 +34,7 @@ struct Args {
     int T;                        // query rows; query / out are [T][Hq][D]
     int q_blocks;                 // query blocks per sequence in the grid
     int prefill_columns;          // (query token, head) columns per work-group
+    int by_length;                // 1: (sequence, kv head) pairs in decreasing length
 };
 
 // Tokens one loop iteration of the tiled kernels covers; partitions are

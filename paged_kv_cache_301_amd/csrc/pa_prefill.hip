@@ -42,6 +42,7 @@
 #include "pa_table.h"
 #include "pa_tile.h"
 #include "pa_rows.h"
+#include "pa_sched.h"
 #include "pa_mfma_core.h"
 
 namespace pa {
@@ -183,7 +184,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(Args a) {
     const int qb = slot % a.q_blocks;
     const int pair = (slot / a.q_blocks) * kXcds + xcd;
     if (pair >= a.S * a.Hkv) return;
-    const int s = pair / a.Hkv;
+    // pairs in decreasing context length (kv head fastest) when the launch
+    // takes several rounds, so the longest contexts start first and it ends
+    // on the short ones
+    const int s = a.by_length
+                      ? sequence_by_length(a.seq_lens, a.S, a.max_blocks * a.B, pair / a.Hkv)
+                      : pair / a.Hkv;
+    if (s < 0) return;   // lengths outside [0, max_blocks * B]: nothing to map
     const int kvh = pair % a.Hkv;
     const int p = blockIdx.y;
 

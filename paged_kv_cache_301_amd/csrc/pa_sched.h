@@ -142,4 +142,39 @@ __device__ __forceinline__ WorkItem decode_work_item(const int32_t *seq_lens, in
     return WorkItem{s, (int)(idx % Hkv), L / part_tokens, true};
 }
 
+// The sequence that comes rank-th in decreasing length order (ties by
+// index; a bijection of [0, S)), found by one wave from the lengths alone,
+// as the second part of the live list above: the largest length v with more
+// than `rank` sequences at least that long, then the sequence among those of
+// length exactly v.  S <= kSchedMaxSeqs; lengths in [0, max_len].
+__device__ __forceinline__ int sequence_by_length(const int32_t *seq_lens, int S, int max_len,
+                                                  int rank) {
+    const int lane = threadIdx.x & 63;
+    int key[kSchedChunks];
+#pragma unroll
+    for (int c = 0; c < kSchedChunks; ++c) {
+        const int s = 64 * c + lane;
+        key[c] = s < S ? seq_lens[s] : -1;
+    }
+    const int nchunks = (S + 63) >> 6;
+    auto count_at_least = [&](int v) -> int {
+        int acc = 0;
+#pragma unroll
+        for (int c = 0; c < kSchedChunks; ++c)
+            if (c < nchunks) acc += key[c] >= v ? 1 : 0;
+        return wave_sum_int(acc);
+    };
+    int lo = 0, hi = max_len;
+    while (lo < hi) {
+        const int mid = lo + ((hi - lo + 1) >> 1);
+        if (count_at_least(mid) > rank) lo = mid;
+        else hi = mid - 1;
+    }
+    const int before = lo < max_len ? count_at_least(lo + 1) : 0;
+    bool pred[kSchedChunks];
+#pragma unroll
+    for (int c = 0; c < kSchedChunks; ++c) pred[c] = key[c] == lo;
+    return select_rank(pred, nchunks, rank - before);
+}
+
 }  // namespace pa
