@@ -501,6 +501,12 @@ def bench_prefill(args, dev):
         over["B"] = args.block_size
     if args.q_heads:
         over["Hq"] = args.q_heads
+    if args.seqs:
+        over["S"] = args.seqs
+    if args.fixed_len:
+        S = args.seqs or workloads.SPECS["prefill"].S
+        over["lens"] = ("fixed", (args.fixed_len,) * S)
+        over["max_len"] = args.fixed_len
     name = args.workload if args.workload in workloads.PREFILL_NEW else "prefill"
     pw = workloads.make_prefill_workload(name, args.new_tokens or None, device=dev, **over)
     w = pw.base
