@@ -321,6 +321,35 @@ def test_prefill_stages_and_determinism():
 
 
 @pytest.mark.gpu
+def test_prefill_many_sequences_longest_first():
+    """A launch of several rounds of work-groups takes its (sequence, kv
+    head) pairs in decreasing context length: 300 ragged sequences (the
+    length search then spans five chunks of 64 lanes), every row against the
+    oracle, the output NaN-filled so that a sequence the order skipped or
+    repeated shows."""
+    from gpu_check import check
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 600, size=300)]
+    lens[5], lens[70], lens[299] = 600, 1, 600     # ties at the top, a one-token context
+    print(f"case: prefill 300 sequences, longest first (lens {min(lens)}..{max(lens)})", flush=True)
+    pw = _small("bf16", 32, 8, 16, lens, 16, seed=31)
+    w = pw.base
+    p = b.plan_prefill(w.S, pw.T, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, pw.max_query_len,
+                       w.dtype)
+    # 64-column work-groups of two waves, four per CU: 2400 of them are
+    # more than the 1024 resident ones
+    assert (w.S * w.Hkv + 7) // 8 * 8 > 1024 and pw.max_query_len * (w.Hq // w.Hkv) <= 64
+    out = torch.full((pw.T, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    b.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, pw.query_start,
+              w.scale, out, max_query_len=pw.max_query_len)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                         pw.query_start, w.scale)
+    check(out, ref, w.dtype, "prefill 300 sequences")
+    assert p["split"] == 0
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("over", [{}, {"Hq": 8, "Hkv": 8}, {"Hq": 64, "Hkv": 1}])
 def test_prefill_full_size_every_row(over):
     """The benchmark's chunked-prefill workload at full size, automatic plan:
