@@ -181,7 +181,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(Args a) {
     // that XCD's L2 instead of each reading them from HBM.  y = partition.
     const int xcd = blockIdx.x % kXcds;
     const int slot = blockIdx.x / kXcds;
-    const int qb = slot % a.q_blocks;
+    // ordered launches also take a pair's query blocks last first: the later
+    // rows of a chunk attend the longer causal contexts
+    const int qb = a.by_length ? a.q_blocks - 1 - slot % a.q_blocks : slot % a.q_blocks;
     const int pair = (slot / a.q_blocks) * kXcds + xcd;
     if (pair >= a.S * a.Hkv) return;
     // pairs in decreasing context length (kv head fastest) when the launch
