@@ -558,6 +558,24 @@ def test_waves_per_item(kernel, Hq, Hkv, B, part, tw):
           f"{kernel} waves part={part} tw={tw}/native")
 
 
+@pytest.mark.parametrize("name,S,L,kernel,tw", [
+    ("gqa_70b", 128, 1500, binding.KERNEL_MFMA, 2), ("mha_7b", 64, 3000, binding.KERNEL_VALU, 4)])
+def test_short_context_waves_automatic(name, S, L, kernel, tw):
+    """Batches of at least 512 (sequence, kv head) pairs whose partition the
+    small-batch rule would halve run one pass on token-waves instead, with at
+    most 1024 tokens a wave: the automatic plan, every row against the
+    oracle, the output NaN-filled."""
+    say(f"case: short-context waves {name} S={S} L={L}")
+    w = workloads.make_workload(name, device=DEV, poison=True, S=S,
+                                lens=("fixed", (L,) * S), max_len=L)
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype)
+    assert p["kernel"] == kernel and p["split"] == 0 and p["token_waves"] == tw
+    out = torch.full((w.S, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale, out)
+    torch.cuda.synchronize()
+    check(out, oracle_full(w), w.dtype, f"short-context waves {name}")
+
+
 def _wave_sweep_case(i):
     """A seeded random shape for the token-wave sweep: kernel family, group,
     kv heads, block size, type, waves, partition and a ragged length mix
