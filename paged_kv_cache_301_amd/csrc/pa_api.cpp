@@ -61,8 +61,10 @@ constexpr long long kValuResidentWaves = 3072;
 // Batches that fill a round only at the table width keep the halving to
 // two rounds: their tables are mostly empty (one round at the table width
 // was slower on 8 sequences of up to 2048 or 4096 tokens, 28.2 -> 29.4 and
-// 57.9 -> 61.2 us, and on 32 of 128 - 8192, 69.8 -> 71.9).
-long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
+// 57.9 -> 61.2 us, and on 32 of 128 - 8192, 69.8 -> 71.9).  The VALU
+// kernel counts its own 3072 slots: 8 MHA sequences of 16000 tokens keep
+// 1024-token partitions, 332.9 / 333.9 us against 341.0 / 342.3 at 2048.
+long long auto_partition(int S, int Hkv, long long max_ctx, int waves, bool valu) {
     if (max_ctx <= kAutoSinglePass) return max_ctx;
     long long part = kAutoPartitionMin;
     while (part * kAutoMaxParts < max_ctx) part *= 2;
@@ -73,7 +75,8 @@ long long auto_partition(int S, int Hkv, long long max_ctx, int waves) {
     if (waves > 1) {
         while (part < max_ctx && 3 * items(part) * waves > 4 * resident) part *= 2;
     } else if (pairs < kMultiWavePairs) {
-        while (part < max_ctx && 3 * items(part) > 4 * resident) {
+        const long long slots = valu ? kValuResidentWaves : resident;
+        while (part < max_ctx && 3 * items(part) > 4 * slots) {
             part *= 2;
             grown = true;
         }
@@ -205,7 +208,7 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
     if (kernel != PA_KERNEL_GENERIC) {
         const long long cap = table_cap(kernel, B);
         const int waves = kernel == PA_KERNEL_MFMA ? (Hq / Hkv + 15) / 16 : 1;
-        long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx, waves);
+        long long part = req > 0 ? req : auto_partition(S, Hkv, max_ctx, waves, kernel == PA_KERNEL_VALU);
         // Token-waves: with at least kMultiWavePairs (sequence, kv head)
         // pairs, a full one-wave partition (not one halved for a small
         // batch) becomes four waves on a partition four times as long, each
