@@ -147,10 +147,13 @@ typedef struct {
 } pa_plan;
 
 /*
- * pa_decode_plan -- resolve the kernel and context partitioning for a shape.
- * Host-only: touches no device and launches nothing.  `cfg` may be NULL
- * (automatic).  Returns the same validation status pa_decode_ex would for
- * these sizes and types.
+ * pa_decode_plan -- resolve the kernel, the context partitioning and the
+ * waves per item for a shape.  Host-only: touches no device and launches
+ * nothing.  `cfg` may be NULL (automatic).  Returns the same validation
+ * status pa_decode_ex would for these sizes and types.  The automatic plan
+ * sees only the table width (max_blocks * B), not the lengths: it sizes
+ * partitions and token-waves so the items of a batch that fills its tables
+ * fill the GPU's resident waves.
  */
 pa_status pa_decode_plan(int S, int Hq, int Hkv, int D, int B, int NB,
                          int max_blocks, pa_dtype dtype, pa_dtype out_dtype,
