@@ -127,10 +127,12 @@ typedef struct {
                              item's tokens, every one streaming every
                              token_waves-th 32-token tile, their softmax
                              states merged in LDS.  Above 1 it needs the VALU
-                             kernel or the matrix-core kernel with at most 16
-                             query heads per kv head, and a block size that is
-                             a multiple of 4 (else PA_ERR_UNSUPPORTED); other
-                             values are PA_ERR_SHAPE.  Decode only: the
+                             kernel with a block size that is a multiple of 4,
+                             or the matrix-core kernel with at most 16 query
+                             heads per kv head (any block size; the automatic
+                             plan keeps blocks of 1 or 2 tokens on one wave)
+                             (else PA_ERR_UNSUPPORTED); other values are
+                             PA_ERR_SHAPE.  Decode only: the
                              multi-token calls accept 0 or 1.                   */
 } pa_config;
 

@@ -135,11 +135,15 @@ long long table_cap(int kernel, int B) {
 
 // Token-waves per item of the VALU kernel and of the matrix-core kernel's
 // one-wave groups (at most 16 heads): each streams every TW-th 32-token tile
-// of the partition, and their softmax states meet in LDS.  Blocks of fewer
-// than 4 tokens keep one wave (their partitions are capped by the LDS table
-// slice anyway).
+// of the partition, and their softmax states meet in LDS.  The VALU kernel's
+// waves need blocks of at least 4 tokens; the matrix-core kernel's also run
+// on the table slice staged in LDS for smaller blocks, though only when asked
+// for (the automatic plan keeps those on one wave: their partitions are
+// capped by the slice, and on 32k-token tables at one kv head per 8 query
+// heads, one-token blocks took 244.2 / 251.1 / 259.0 us a cold step on 1 / 2
+// / 4 waves, two-token blocks 227.8 / 252.8 / 227.3).
 bool multi_wave_items(int kernel, int G, int B) {
-    return (kernel == PA_KERNEL_VALU || (kernel == PA_KERNEL_MFMA && G <= 16)) && B % 4 == 0;
+    return kernel == PA_KERNEL_VALU ? B % 4 == 0 : kernel == PA_KERNEL_MFMA && G <= 16;
 }
 
 // Waves for a partition the planner made multi-wave: at most 1024 tokens
@@ -225,7 +229,7 @@ pa_status make_plan(int S, int Hq, int Hkv, int D, int B, int NB, int max_blocks
         // pairs) 226.3 -> 232.8.  A partition halved for a small batch stays
         // on one wave (8 sequences of up to 2048 tokens: 27.3 against
         // 29.4-31.8 on four).
-        if (req == 0 && multi_wave_items(kernel, G, B) && (long long)S * Hkv >= kMultiWavePairs) {
+        if (req == 0 && multi_wave_items(kernel, G, B) && B % 4 == 0 && (long long)S * Hkv >= kMultiWavePairs) {
             if (part >= kAutoPartitionMin && part < max_ctx) {
                 part *= 4;
                 multi = true;

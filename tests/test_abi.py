@@ -128,6 +128,13 @@ def test_plans():
     p = b.plan(64, 32, 32, 128, 16, 15360, 1024, torch.bfloat16, partition_tokens=4096,
                token_waves=2)
     assert p["partition_tokens"] == 4096 and p["token_waves"] == 2
+    # blocks of one or two tokens: waves on the matrix-core kernel only when
+    # asked; the automatic plan keeps them on one wave at any batch size
+    p = b.plan(64, 32, 8, 128, 1, 1 << 20, 16384, torch.bfloat16, token_waves=4)
+    assert p["kernel"] == b.KERNEL_MFMA and p["partition_tokens"] <= 1024 and p["token_waves"] == 4
+    for B in (1, 2):
+        p = b.plan(128, 64, 8, 128, B, 1 << 20, 32768 // B, torch.bfloat16)   # 1024 pairs
+        assert p["kernel"] == b.KERNEL_MFMA and p["token_waves"] == 1
     assert b.plan(64, 32, 32, 128, 16, 15360, 256, torch.bfloat16,
                   kernel="mfma")["kernel"] == b.KERNEL_MFMA
     assert b.plan(8, 16, 8, 128, 16, 645, 128, torch.float16)["kernel"] == b.KERNEL_VALU

@@ -621,3 +621,32 @@ def test_token_wave_sweep(i):
         if L == 0:
             assert torch.equal(out[s], torch.zeros_like(out[s]))
     check(run(w, workspace=ws, **kw), ref, DT[dtype], f"wave sweep {i}/native")
+
+
+@pytest.mark.parametrize("Hq,Hkv,B,part,tw", [
+    (8, 8, 1, 1024, 2), (8, 8, 1, 1024, 4), (32, 8, 2, 2048, 4), (16, 2, 1, 512, 4),
+    (128, 8, 1, 1024, 2), (64, 8, 2, 256, 4), (8, 1, 2, 1024, 2)])
+def test_token_waves_small_blocks(Hq, Hkv, B, part, tw):
+    """Matrix-core items on two or four waves with blocks of one or two
+    tokens, where every lane looks its block up in the partition's slice of
+    the table staged in LDS by all the work-group's waves: every row against
+    the oracle, the workspace NaN-filled, with empty, one-token, ragged and
+    partition-multiple contexts."""
+    say(f"case: small-block waves Hq={Hq} Hkv={Hkv} B={B} part={part} tw={tw}")
+    lens = (1, 33, 1000, 4096, 5000, 2047, 0, 8191, part, 2 * part + 1)
+    spec = workloads.WorkloadSpec("token_waves_small_blocks", S=len(lens), Hq=Hq, Hkv=Hkv, D=128,
+                                  B=B, dtype="bf16", lens=("fixed", lens), max_len=8192,
+                                  pool=("free", 0.2), seed=7300 + part // 256 + B + tw)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    kw = dict(kernel="mfma", partition_tokens=part, token_waves=tw)
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, **kw)
+    assert p["kernel"] == binding.KERNEL_MFMA and p["partition_tokens"] == part
+    assert p["token_waves"] == tw
+    ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+          if p["workspace_bytes"] else None)
+    ref = oracle_full(w)
+    out = run(w, out_dtype=torch.float32, workspace=ws, **kw)
+    check(out, ref, torch.bfloat16, f"small-block waves B={B} part={part} tw={tw}")
+    assert torch.equal(out[6], torch.zeros_like(out[6]))
+    check(run(w, workspace=ws, **kw), ref, torch.bfloat16,
+          f"small-block waves B={B} part={part} tw={tw}/native")

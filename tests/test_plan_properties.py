@@ -126,14 +126,14 @@ def test_decode_plan_properties(sh):
     assert forced == b.KERNEL_AUTO or p.kernel == forced
     assert supports(p.kernel, Hq, Hkv, D, B, dt)
     G = Hq // Hkv
-    multi_ok = B % 4 == 0 and (p.kernel == b.KERNEL_VALU or (p.kernel == b.KERNEL_MFMA and G <= 16))
+    multi_ok = (p.kernel == b.KERNEL_VALU and B % 4 == 0) or (p.kernel == b.KERNEL_MFMA and G <= 16)
     assert sh["tw"] <= 1 or multi_ok
     if sh["tw"]:
         assert p.token_waves == sh["tw"]
     else:
         assert p.token_waves in (1, 2, 4)
         if p.token_waves > 1:
-            assert multi_ok and req == 0 and S * Hkv >= 512
+            assert multi_ok and B % 4 == 0 and req == 0 and S * Hkv >= 512
             assert p.partition_tokens > 512 * p.token_waves   # at most 1024 tokens a wave
     if p.kernel == b.KERNEL_GENERIC:
         assert p.split == 0 and p.workspace_bytes == 0 and p.max_partitions == 1
