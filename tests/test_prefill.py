@@ -6,7 +6,8 @@ five-token prefill (each row's closed form; the last row is the printed
 torch's SDPA routine, and to causality itself (NaN in every later token
 leaves a row unchanged).  Host validation of the C ABI.
 GPU: the library against the oracle on identical inputs (both kernels, every
-group size, block sizes 1..32, forced partitions, ragged chunks), an exact
+group size, block sizes 1..32, forced partitions, ragged chunks, and a seeded
+sweep of random shapes over all of these), an exact
 needle check of positions, staged calls, and the benchmark-sized workload on
 sampled rows.
 """
@@ -369,3 +370,63 @@ def test_prefill_full_size_every_row(over):
     ref = oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
                          pw.query_start, w.scale)
     check(out, ref, w.dtype, "prefill full")
+
+
+def _prefill_sweep_case(i):
+    """A seeded random shape for the multi-token sweep: kernel, group, kv
+    heads, block size, type, partition, a ragged length mix and new-token
+    counts that reach each work-group width (64, 128 or 256 columns), with
+    sequences that take no new token.  The oracle's work (rows x heads x
+    attended tokens) is kept to about a second."""
+    rng = np.random.default_rng(9500 + i)
+    kernel = "generic" if i % 8 == 7 else "mfma"
+    dt = ("bf16", "f16")[(i // 2) % 2]
+    G = int(rng.choice((1, 2, 4, 8, 16, 32, 64)))
+    Hkv = int(rng.choice((1, 2) if G >= 32 else (1, 2, 4)))
+    B = int(rng.choice((1, 2, 4, 8, 16, 32)))
+    if kernel == "generic" and B == 1:
+        B = 3                                  # the generic kernel takes any block size
+    part = 0 if rng.random() < 0.4 else 32 * int(rng.integers(2, 33))
+    S = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(1, 2001, size=S)]
+    for k in range(min(S, 2)):
+        lens[int(rng.integers(0, S))] = int(rng.choice((1, 32, 33, max(part, 64), 2000)))
+    cap = int(rng.choice((2, 8, 64, 300)))     # longest chunk: 64, 128 or 256 columns
+    new = [int(rng.integers(0, min(L, cap) + 1)) for L in lens]
+    j = int(rng.integers(0, S))
+    new[j] = min(lens[j], cap)                 # one chunk reaches the cap
+    if sum(new) == 0:
+        new[0] = 1
+    budget = 2.5e8 / (G * Hkv)                 # attended (row, token) pairs per head
+    while sum(n * L for n, L in zip(new, lens)) > budget:
+        new = [n // 2 for n in new]
+        if sum(new) == 0:
+            new[0] = 1
+            break
+    return kernel, dt, G * Hkv, Hkv, B, part, tuple(lens), tuple(new)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(32))
+def test_prefill_sweep(i):
+    """Random shapes through the multi-token path: every row against the
+    oracle, in fp32 and in the native type, the workspace NaN-filled."""
+    from gpu_check import check
+    kernel, dt, Hq, Hkv, B, part, lens, new = _prefill_sweep_case(i)
+    print(f"case: prefill sweep {i}: {kernel} {dt} Hq={Hq} Hkv={Hkv} B={B} part={part} "
+          f"lens={lens} new={new}", flush=True)
+    D = 128 if kernel == "mfma" else 64
+    pw = _small(dt, Hq, Hkv, B, lens, new, seed=9600 + i, D=D)
+    w = pw.base
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    p = b.plan_prefill(w.S, pw.T, Hq, Hkv, D, B, w.NB, w.max_blocks, pw.max_query_len, tdt,
+                       kernel=kernel, partition_tokens=part)
+    assert p["kernel"] == b.KERNELS[kernel]
+    ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+          if p["workspace_bytes"] else None)
+    ref = _oracle_full(pw)
+    for od in (torch.float32, tdt):
+        out = b.prefill_workload(pw, out_dtype=od, kernel=kernel, partition_tokens=part,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        check(out, ref, tdt, f"prefill sweep {i}/{od}")
