@@ -650,3 +650,60 @@ def test_token_waves_small_blocks(Hq, Hkv, B, part, tw):
     assert torch.equal(out[6], torch.zeros_like(out[6]))
     check(run(w, workspace=ws, **kw), ref, torch.bfloat16,
           f"small-block waves B={B} part={part} tw={tw}/native")
+
+
+def _decode_sweep_case(i):
+    """A seeded random decode call: kernel family (or the automatic choice),
+    a shape that family supports (the generic kernel: any head size up to
+    256, block size and type), partition (automatic or forced), a ragged
+    length mix with empty, one-token, tile-edge and partition-multiple
+    contexts, and a table a little wider than the longest context."""
+    rng = np.random.default_rng(9800 + i)
+    kernel = ("auto", "generic", "valu", "mfma")[i % 4]
+    if kernel == "generic" or (kernel == "auto" and rng.random() < 0.25):
+        D = int(rng.choice((8, 64, 80, 96, 128, 192, 256)))
+        dtype = str(rng.choice(("f32", "f16", "bf16")))
+        B = int(rng.choice((1, 2, 3, 5, 8, 16, 24, 32)))
+        G = int(rng.choice((1, 2, 3, 4, 6, 8, 16)))
+        Hkv = int(rng.choice((1, 2, 4)))
+    else:
+        D = 128
+        dtype = str(rng.choice(("f16", "bf16")))
+        B = int(rng.choice((1, 2, 4, 8, 16, 32, 64)))
+        G = int(rng.choice((1, 2, 4, 8) if kernel == "valu" else (1, 2, 4, 8, 16, 32, 64)))
+        Hkv = int(rng.choice((1, 2, 4) if G >= 16 else (1, 2, 4, 8)))
+    part = 0 if kernel == "generic" or rng.random() < 0.5 else 32 * int(rng.integers(1, 65))
+    S = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(0, 3001, size=S)]
+    special = (0, 1, 31, 32, 33, max(part, 32), 2 * max(part, 32) + 1, 3000)
+    for k in range(min(S, 3)):
+        lens[int(rng.integers(0, S))] = int(rng.choice(special))
+    max_len = max(max(lens), 1) + int(rng.integers(0, 2 * B + 1))
+    return kernel, D, dtype, B, G * Hkv, Hkv, part, lens, max_len
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_decode_sweep(i):
+    """Random decode calls through every kernel family and the automatic
+    plan: every row against the oracle in fp32 and in the native type, the
+    workspace NaN-filled, empty contexts exactly zero."""
+    kernel, D, dtype, B, Hq, Hkv, part, lens, max_len = _decode_sweep_case(i)
+    say(f"case: decode sweep {i}: {kernel} D={D} {dtype} B={B} Hq={Hq} Hkv={Hkv} part={part} "
+        f"lens={lens} max_len={max_len}")
+    spec = workloads.WorkloadSpec("decode_sweep", S=len(lens), Hq=Hq, Hkv=Hkv, D=D, B=B,
+                                  dtype=dtype, lens=("fixed", tuple(lens)), max_len=max_len,
+                                  pool=("free", 0.2), seed=9900 + i)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    kw = dict(kernel=kernel, partition_tokens=part)
+    p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, **kw)
+    if kernel != "auto":
+        assert p["kernel"] == binding.KERNELS[kernel]
+    ws = (torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+          if p["workspace_bytes"] else None)
+    ref = oracle_full(w)
+    for od in (torch.float32, DT[dtype]):
+        out = run(w, out_dtype=od, workspace=ws, **kw)
+        check(out, ref, DT[dtype], f"decode sweep {i}/{od}")
+        for s, L in enumerate(lens):
+            if L == 0:
+                assert torch.equal(out[s], torch.zeros_like(out[s]))
