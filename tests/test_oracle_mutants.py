@@ -41,6 +41,12 @@ MUTANTS = {
     "prefill_sequence_row": ("t, pos + 1, scale, out", "s, pos + 1, scale, out"),
     "prefill_future_visible": ("t, pos + 1, scale, out", "t, seq_lens[s], scale, out"),
     "score_sign": ("acc += qv[d] * K", "acc -= qv[d] * K"),
+    "write_offset_dropped": ("* B + offset) * (size_t)D * esz;", "* B + 0) * (size_t)D * esz;"),
+    "write_page_layout": ("(((size_t)block * Hkv + h) * B + offset)",
+                          "(((size_t)block * B + offset) * Hkv + h)"),
+    "write_key_into_values": ("memcpy((char *)value_cache + dst, (const char *)value + src",
+                              "memcpy((char *)value_cache + dst, (const char *)key + src"),
+    "write_block_zero": ("long long block = slot / B, offset", "long long block = 0 * slot / B, offset"),
 }
 
 
@@ -110,6 +116,13 @@ def _battery():
                         pk["block_tables"], pk["seq_lens"], 1.0)
     if not np.allclose(out[0, 0], V[L - 1, 0].double().numpy(), atol=1e-12):
         failed.append("large_scores")
+    # a decode-step write, then attention over the grown contexts
+    from test_kv_write import append_then_attend_error
+    try:
+        if not append_then_attend_error(torch.float32) < 1e-12:
+            failed.append("append_then_attend")
+    except ValueError:
+        failed.append("append_raised")
     # conversions (a sample of bit patterns)
     for bits in (0x3C00, 0x0001, 0x7BFF, 0xC000, 0x3555):
         ref = torch.tensor([bits], dtype=torch.int32).to(torch.int16).view(torch.float16).item()
