@@ -40,7 +40,12 @@ def _page_example(mgr_cls):
 
 @pytest.mark.parametrize("impl", ["oracle", "library"])
 def test_copy_on_write_example(impl):
-    m, other, a, bb, slots, cp = _page_example(BlockManager if impl == "oracle" else b.BlockPool)
+    cow_example_checks(BlockManager if impl == "oracle" else b.BlockPool, impl)
+
+
+def cow_example_checks(mgr_cls, impl="oracle"):
+    """The page's copy-on-write example, step by step (slots, tables, counts)."""
+    m, other, a, bb, slots, cp = _page_example(mgr_cls)
     tab = (lambda s: m.table(s)) if impl == "oracle" else (lambda s: m.export([s], 3, -1)[0][0].tolist())
     assert slots == [4, 5, 0, 1, 2] and cp is None
     assert tab(a) == [2, 0, 1] and tab(bb) == [2, 0, 1]
@@ -58,10 +63,14 @@ def test_copy_on_write_example(impl):
 
 
 def test_copy_on_write_example_data():
+    cow_example_data_checks(BlockManager, oracle_copy)
+
+
+def cow_example_data_checks(mgr_cls, copy_fn):
     """The copied block holds [k5, v5] and gets k6 in slot 1; B's k6 lands in
     block 1; each candidate's attention equals unpaged attention over its own
     six tokens."""
-    m, other, a, bb, slots, _ = _page_example(BlockManager)
+    m, other, a, bb, slots, _ = _page_example(mgr_cls)
     g = torch.Generator().manual_seed(0)
     D = 4
     kc = torch.full((9, 1, 2, D), float("nan"), dtype=torch.float64)
@@ -75,7 +84,7 @@ def test_copy_on_write_example_data():
     for s in (a, bb):
         sl, cp = m.append(s, 1)
         if cp:
-            kc, vc = oracle_copy(kc, vc, [cp])
+            kc, vc = copy_fn(kc, vc, [cp])
         kc, vc, n = oracle.write_kv(k6[s], v6[s], torch.tensor(sl, dtype=torch.int32), kc, vc)
         assert n == 1
     assert torch.equal(kc[4, 0, 0], prompt_k[4, 0].float()) and torch.equal(kc[4, 0, 1], k6[a][0, 0])
@@ -159,7 +168,13 @@ def _apply(m, op, live, is_oracle):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_oracle_invariants_random_ops(seed):
-    m = BlockManager(24, 4)
+    random_ops_checks(BlockManager, seed)
+
+
+def random_ops_checks(mgr_cls, seed):
+    """Random creates, forks, releases, appends and batches; the invariants
+    hold after every op."""
+    m = mgr_cls(24, 4)
     live = []
     for op in _random_ops(seed, 24, 4, 400):
         _apply(m, op, live, True)
@@ -167,7 +182,12 @@ def test_oracle_invariants_random_ops(seed):
 
 
 def test_oracle_batch_is_all_or_nothing():
-    m = BlockManager(3, 2)
+    batch_checks(BlockManager)
+
+
+def batch_checks(mgr_cls):
+    """A batch that runs out of blocks changes nothing; a smaller one copies."""
+    m = mgr_cls(3, 2)
     s0 = m.create()
     m.append(s0, 1)
     s1 = m.fork(s0)
@@ -232,13 +252,19 @@ def test_library_pool_errors():
 
 
 def test_oracle_copy_blocks():
+    copy_checks(oracle_copy)
+
+
+def copy_checks(copy_fn):
+    """Live pairs copied, skipped pairs (src == dst, out of range) ignored,
+    a copy target that is another copy's source refused."""
     kc = torch.arange(5 * 2 * 3 * 4, dtype=torch.float32).reshape(5, 2, 3, 4)
     vc = -kc
-    k2, v2 = oracle_copy(kc, vc, [(1, 3), (4, 0), (2, 2), (7, 1), (0, -1)])
+    k2, v2 = copy_fn(kc, vc, [(1, 3), (4, 0), (2, 2), (7, 1), (0, -1)])
     assert torch.equal(k2[3], kc[1]) and torch.equal(k2[0], kc[4]) and torch.equal(v2[3], vc[1])
     assert torch.equal(k2[[1, 2, 4]], kc[[1, 2, 4]])
     with pytest.raises(AssertionError):
-        oracle_copy(kc, vc, [(1, 3), (3, 4)])
+        copy_fn(kc, vc, [(1, 3), (3, 4)])
 
 
 def test_copy_blocks_validation():
