@@ -4,7 +4,8 @@
   empty contexts, every kernel family;
 * contexts that fill their block table exactly (the last used entry is the
   table's last column), with single-pass and split plans;
-* the generic kernel at the smallest, an odd and the largest head size.
+* the generic kernel at the smallest, an odd and the largest head size;
+* contexts of 300k and 512k tokens, at blocks of 16 tokens and of one.
 """
 import numpy as np
 import pytest
@@ -79,3 +80,28 @@ def test_generic_head_sizes(D, dt):
         ref = oracle.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
                             w.scale)
         check(out, ref, dtype, f"generic/D{D}/{dt}")
+
+
+@pytest.mark.parametrize("B", [16, 1])
+def test_long_contexts(B):
+    """A 512k-token context beside a 300k-token and a one-token one: the
+    automatic plan (hundreds of partitions for this small batch, merged by the
+    wide combine), forced 1024-token partitions (513 per row), the VALU kernel,
+    and four waves per item; every row against the oracle, the workspace
+    NaN-filled."""
+    lens = (524288, 300001, 1)
+    say(f"case: long contexts B={B} lens={lens}")
+    spec = workloads.WorkloadSpec("long_context", S=len(lens), Hq=32, Hkv=8, D=128, B=B,
+                                  dtype="bf16", lens=("fixed", lens), max_len=max(lens) + B,
+                                  pool=("free", 0.1), seed=31 + B)
+    w = workloads.make_workload(spec, device=DEV, poison=True)
+    ref = oracle.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens, w.scale)
+    for kw in (dict(), dict(kernel="mfma", partition_tokens=1024), dict(kernel="valu"),
+               dict(kernel="mfma", partition_tokens=1024 if B < 4 else 8192, token_waves=4)):
+        p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, **kw)
+        say(f"  plan {kw}: {p}")
+        assert p["split"] == 1 and p["max_partitions"] > 32
+        ws = torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV)
+        out = binding.decode_workload(w, out_dtype=torch.float32, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        check(out, ref, w.dtype, f"long/B{B}/{kw}")
