@@ -36,21 +36,23 @@ def _raw_ex(lib, w, out, cfg, ws, stream):
 
 
 CASES = [
-    # (workload, overrides of the first call, overrides of the second, kernel, partition)
-    ("mha_7b", {}, {"S": 9, "seed": 31}, "auto", 0),
-    ("gqa_70b", {}, {"S": 20, "seed": 32}, "auto", 0),
-    ("gqa_long", {"B": 16}, {"S": 3, "seed": 33, "B": 16}, "auto", 0),
-    ("mqa", {}, {"S": 40, "seed": 34}, "auto", 0),
-    ("mha_small", {}, {"S": 3, "seed": 35}, "valu", 64),
+    # (workload, overrides of the first call, overrides of the second, kernel, partition,
+    #  waves per item: 0 = the plan's choice)
+    ("mha_7b", {}, {"S": 9, "seed": 31}, "auto", 0, 0),
+    ("gqa_70b", {}, {"S": 20, "seed": 32}, "auto", 0, 0),
+    ("gqa_long", {"B": 16}, {"S": 3, "seed": 33, "B": 16}, "auto", 0, 0),
+    ("mqa", {}, {"S": 40, "seed": 34}, "auto", 0, 0),
+    ("mha_small", {}, {"S": 3, "seed": 35}, "valu", 64, 0),
+    ("gqa_long", {"B": 1}, {"S": 3, "seed": 36, "B": 1}, "mfma", 0, 4),
 ]
 
 
-@pytest.mark.parametrize("name,first,second,kernel,part", CASES)
-def test_noalloc_matches_workspace_entry_point(name, first, second, kernel, part):
-    print(f"case: no-allocation entry point, {name} {first} then {second}", flush=True)
+@pytest.mark.parametrize("name,first,second,kernel,part,tw", CASES)
+def test_noalloc_matches_workspace_entry_point(name, first, second, kernel, part, tw):
+    print(f"case: no-allocation entry point, {name} {first} then {second} tw={tw}", flush=True)
     lib = binding.load()
     stream = torch.cuda.current_stream(DEV)
-    cfg = binding.PaConfig(binding.KERNELS[kernel], part, 0, 0, 0)
+    cfg = binding.PaConfig(binding.KERNELS[kernel], part, 0, 0, 0, tw)
     for over in (first, second):
         over = dict(over)
         seed = over.pop("seed", None)
@@ -58,7 +60,8 @@ def test_noalloc_matches_workspace_entry_point(name, first, second, kernel, part
             over["seed"] = seed
         w = workloads.make_workload(name, device=DEV, poison=True, **over)
         p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype,
-                         torch.float32, kernel=kernel, partition_tokens=part)
+                         torch.float32, kernel=kernel, partition_tokens=part, token_waves=tw)
+        assert tw == 0 or p["token_waves"] == tw
         assert p["workspace_bytes"] <= binding.NOALLOC_SCRATCH_BYTES
         ws = (torch.empty(p["workspace_bytes"], dtype=torch.uint8, device=DEV)
               if p["workspace_bytes"] else None)
@@ -74,9 +77,9 @@ def test_noalloc_matches_workspace_entry_point(name, first, second, kernel, part
     # the binding's wrapper, native output type
     o = torch.empty_like(w.query)
     binding.decode_noalloc(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                           w.scale, o, kernel=kernel, partition_tokens=part)
+                           w.scale, o, kernel=kernel, partition_tokens=part, token_waves=tw)
     ref = binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                         w.scale, kernel=kernel, partition_tokens=part)
+                         w.scale, kernel=kernel, partition_tokens=part, token_waves=tw)
     torch.cuda.synchronize()
     assert torch.equal(o, ref)
 
