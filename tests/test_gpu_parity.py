@@ -707,3 +707,49 @@ def test_decode_sweep(i):
         for s, L in enumerate(lens):
             if L == 0:
                 assert torch.equal(out[s], torch.zeros_like(out[s]))
+
+
+def test_concurrent_streams():
+    """Calls in flight at once on three streams, each with its own workspace
+    and output (the library keeps no per-call state outside them): decode on
+    both kernel families and a multi-token call, issued back to back with no
+    synchronisation between them, every row against the oracle afterwards."""
+    say("case: concurrent streams")
+    specs = [workloads.WorkloadSpec("conc_a", S=12, Hq=32, Hkv=32, D=128, B=16, dtype="bf16",
+                                    lens=("uniform", 1, 3000), max_len=3008, pool=("free", 0.2),
+                                    seed=501),
+             workloads.WorkloadSpec("conc_b", S=20, Hq=64, Hkv=8, D=128, B=8, dtype="f16",
+                                    lens=("uniform", 1, 5000), max_len=5008, pool=("free", 0.2),
+                                    seed=502)]
+    ws_ = [workloads.make_workload(sp, device=DEV, poison=True) for sp in specs]
+    pspec = workloads.WorkloadSpec("conc_c", S=6, Hq=32, Hkv=8, D=128, B=16, dtype="bf16",
+                                   lens=("fixed", (700, 1, 2000, 129, 64, 1500)), max_len=2016,
+                                   pool=("free", 0.2), seed=503)
+    pw = workloads.make_prefill_workload(pspec, (300, 1, 64, 0, 64, 7), device=DEV, poison=True)
+    outs, wss = [], []
+    for w, part in zip(ws_, (256, 512)):
+        p = binding.plan(w.S, w.Hq, w.Hkv, w.D, w.B, w.NB, w.max_blocks, w.dtype, torch.float32,
+                         partition_tokens=part)
+        assert p["split"] == 1
+        wss.append(torch.full((p["workspace_bytes"] // 4,), float("nan"), device=DEV))
+        outs.append(torch.full((w.S, w.Hq, w.D), float("nan"), device=DEV))
+    pb = pw.base
+    pp = binding.plan_prefill(pb.S, pw.T, pb.Hq, pb.Hkv, pb.D, pb.B, pb.NB, pb.max_blocks,
+                              pw.max_query_len, pb.dtype, torch.float32, partition_tokens=256)
+    pws = torch.full((max(pp["workspace_bytes"], 256) // 4,), float("nan"), device=DEV)
+    pout = torch.full((pw.T, pb.Hq, pb.D), float("nan"), device=DEV)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(DEV) for _ in range(3)]
+    for rep in range(3):
+        for w, out, ws, part, st in zip(ws_, outs, wss, (256, 512), streams):
+            binding.decode(w.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
+                           w.scale, out, partition_tokens=part, workspace=ws, stream=st)
+        binding.prefill(pw.query, pb.key_cache, pb.value_cache, pb.block_tables, pb.seq_lens,
+                        pw.query_start, pb.scale, pout, max_query_len=pw.max_query_len,
+                        partition_tokens=256, workspace=pws, stream=streams[2])
+    torch.cuda.synchronize()
+    for w, out in zip(ws_, outs):
+        check(out, oracle_full(w), w.dtype, f"concurrent {w.spec.name}")
+    ref = oracle.prefill(pw.query, pb.key_cache, pb.value_cache, pb.block_tables, pb.seq_lens,
+                         pw.query_start, pb.scale)
+    check(pout, ref, pb.dtype, "concurrent prefill")
