@@ -540,10 +540,19 @@ def bench_prefill(args, dev):
     c_ms = time_loop(combine, args.steps, stream)[1] if plan["split"] else 0.0
     flops = pw.flops()
     tf = flops / (step_ms * 1e-3) / 1e12
-    achieved = flops / (k_ms * 1e-3) / 1e12
     kname = {1: "generic", 3: "mfma"}[plan["kernel"]]
     dts = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype]
-    peak = MFMA_PEAK_TFLOPS.get(dts, 157.3)
+    # the roofline that binds: the matrix cores for long chunks, HBM for a
+    # few new tokens per sequence (the unique K+V the chunks attend, read once)
+    kv = w.unique_kv_bytes() if w.spec.prefix_tokens else w.kv_bytes()
+    flop_peak = MFMA_PEAK_TFLOPS.get(dts, 157.3)
+    hbm_bound = kv / (HBM_PEAK_GBS * 1e9) > flops / (flop_peak * 1e12)
+    if hbm_bound:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = kv / (k_ms * 1e-3) / 1e9
+    else:
+        bound, unit, peak = "mfma", "TFLOP/s", flop_peak
+        achieved = flops / (k_ms * 1e-3) / 1e12
     print(f"[bench] prefill: S={w.S} T={pw.T} Hq={w.Hq} Hkv={w.Hkv} B={w.B} ctx={int(w.lens.sum())} "
           f"plan {plan}; kernel {k_ms * 1e3:.1f} us, combine {c_ms * 1e3:.1f} us, step {step_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -557,8 +566,8 @@ def bench_prefill(args, dev):
                    "new_tokens_per_seq": int(pw.max_query_len), "flops": flops, "kernel": kname,
                    "partition_tokens": plan["partition_tokens"], "split": bool(plan["split"])},
         "kernel_us": {"partitions": round(k_ms * 1e3, 2), "combine": round(c_ms * 1e3, 2)},
-        "roofline": {"bound": "mfma", "kernel": f"pa_prefill_{kname}", "achieved": round(achieved, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "roofline": {"bound": bound, "kernel": f"pa_prefill_{kname}", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "kv_bytes": kv,
                      "traffic": recorded_traffic(f"pa_prefill_{kname}", record_key(f"prefill_{name}", args), w.B,
                                                  plan["partition_tokens"])},
     }
