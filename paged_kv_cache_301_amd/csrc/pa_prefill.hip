@@ -18,7 +18,9 @@
 // tokens, or one token of a wide group) the work-group has two waves and 64
 // columns instead, so no block is more than half empty by construction
 // (measured: 4 new tokens on the 16-sequence batch 104 -> 70 us, on the
-// 128-sequence 8-head-group batch 366 -> 334 us).  When the longest chunk
+// 128-sequence 8-head-group batch 366 -> 334 us), and a 16-column group
+// without a query row skips both products and the softmax (that batch's
+// kernel 73 -> 63 us).  When the longest chunk
 // fills 256 columns it has eight waves and 256 columns: each staged
 // sub-tile then serves twice the query rows, which halves the re-reads of
 // a sequence's context by its query blocks (HBM reads 2.2 -> 1.4 GB per
@@ -73,12 +75,15 @@ __device__ __forceinline__ void stage_part(const KVTileN<NL> &tile, uint4 *klds,
 // MASK: some column may not see every token of the sub-tile (lim[j]: tokens
 // column group j's lane may see); without it no score is masked, which is
 // every sub-tile below the block's first query position.  sc: the score
-// scale in exp2 units, positive (see signed_query).
-template <typename T, bool MASK>
+// scale in exp2 units, positive (see signed_query).  SKIP: a group none of
+// whose columns is a query row (live[j] false, wave-uniform) is left out;
+// its state stays empty and it writes nothing.
+template <typename T, bool MASK, bool SKIP>
 __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
                                                const typename Mfma<T>::Vec (&qf)[kGroups][4],
                                                const uint4 *klds, const uint4 *vlds, int t0,
-                                               const int (&lim)[kGroups], int g, int i, float sc) {
+                                               const int (&lim)[kGroups], const bool (&live)[kGroups],
+                                               int g, int i, float sc) {
     using M = Mfma<T>;
     using Vec = typename M::Vec;
     // K fragments: A operand = chunk 4kk + g of row 16h + i (swizzle swz_k = i)
@@ -94,6 +99,7 @@ __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             acc[j][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (SKIP && !live[j]) continue;          // uniform
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) acc[j][h] = M::mma(kf[h][kk], qf[j][kk], acc[j][h]);
         }
@@ -115,6 +121,11 @@ __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
     bool grow_any = false;
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
+        if (SKIP && !live[j]) {                      // uniform: no query row here
+            mt[j] = kNegInf;
+            grow[j] = false;
+            continue;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float v = acc[j][e >> 2][e & 3];
@@ -146,6 +157,7 @@ __device__ __forceinline__ void subtile_groups(MfmaState<T> (&st)[kGroups],
     }
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
+        if (SKIP && !live[j]) continue;              // uniform
         // a column that has seen no token yet keeps zero weights
         const float mneg = st[j].m == kNegInf ? 0.f : -st[j].m;
         float p[8];
@@ -239,6 +251,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(Args a) {
         }
     }
 
+    // groups with at least one query row (wave-uniform); the two-wave
+    // work-groups of few-token calls leave the others out
+    bool live[kGroups];
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) live[j] = __builtin_amdgcn_ballot_w64(ok[j]) != 0;
+    constexpr bool kSkip = NW == 2;
+
     MfmaState<T> st[kGroups];
 #pragma unroll
     for (int j = 0; j < kGroups; ++j) {
@@ -288,14 +307,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(Args a) {
         __builtin_amdgcn_sched_barrier(0);
         stage_part(ra, klds[0], vlds[0], k0, g, i);
         __syncthreads();
-        subtile_groups<T, MASK>(st, qf, klds[0], vlds[0], t0, lim_eff, g, i, sc);
+        subtile_groups<T, MASK, kSkip>(st, qf, klds[0], vlds[0], t0, lim_eff, live, g, i, sc);
         __builtin_amdgcn_sched_barrier(0);
         ctx.load(ra, t0 + 64, k0);
         __builtin_amdgcn_sched_barrier(0);
         if (it + 1 < niter) {
             stage_part(rb, klds[1], vlds[1], k0, g, i);
             __syncthreads();
-            subtile_groups<T, MASK>(st, qf, klds[1], vlds[1], t0 + 32, lim_eff, g, i, sc);
+            subtile_groups<T, MASK, kSkip>(st, qf, klds[1], vlds[1], t0 + 32, lim_eff, live, g, i,
+                                           sc);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
