@@ -144,6 +144,17 @@ def source_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
+def prefill_roofline(kv_bytes: int, flops: int, dtype: str, kernel_s: float):
+    """The roofline that binds a multi-token call: HBM when reading the unique
+    K+V once at the HBM peak takes longer than its flops at the type's dense
+    matrix-core peak (a few new tokens per sequence), else the matrix cores.
+    Returns (bound, achieved, peak, unit) for a kernel time of kernel_s."""
+    flop_peak = MFMA_PEAK_TFLOPS.get(dtype, 157.3)
+    if kv_bytes / (HBM_PEAK_GBS * 1e9) > flops / (flop_peak * 1e12):
+        return "hbm", kv_bytes / kernel_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    return "mfma", flops / kernel_s / 1e12, flop_peak, "TFLOP/s"
+
+
 def record_key(workload: str, args) -> str:
     """Workload name of a traffic record: the named workload plus the
     overrides that change its shape (query heads, new tokens per sequence)."""
@@ -542,17 +553,9 @@ def bench_prefill(args, dev):
     tf = flops / (step_ms * 1e-3) / 1e12
     kname = {1: "generic", 3: "mfma"}[plan["kernel"]]
     dts = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[w.dtype]
-    # the roofline that binds: the matrix cores for long chunks, HBM for a
-    # few new tokens per sequence (the unique K+V the chunks attend, read once)
+    # the unique K+V the chunks attend, read once
     kv = w.unique_kv_bytes() if w.spec.prefix_tokens else w.kv_bytes()
-    flop_peak = MFMA_PEAK_TFLOPS.get(dts, 157.3)
-    hbm_bound = kv / (HBM_PEAK_GBS * 1e9) > flops / (flop_peak * 1e12)
-    if hbm_bound:
-        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
-        achieved = kv / (k_ms * 1e-3) / 1e9
-    else:
-        bound, unit, peak = "mfma", "TFLOP/s", flop_peak
-        achieved = flops / (k_ms * 1e-3) / 1e12
+    bound, achieved, peak, unit = prefill_roofline(kv, flops, dts, k_ms * 1e-3)
     print(f"[bench] prefill: S={w.S} T={pw.T} Hq={w.Hq} Hkv={w.Hkv} B={w.B} ctx={int(w.lens.sum())} "
           f"plan {plan}; kernel {k_ms * 1e3:.1f} us, combine {c_ms * 1e3:.1f} us, step {step_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)

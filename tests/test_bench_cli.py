@@ -92,3 +92,20 @@ def test_headline_workloads_have_current_records(kernel, workload, B):
         pytest.skip(f"traffic record for {kernel} {workload} predates the current kernel "
                     "sources: profile again")
     assert got > 0
+
+
+def test_prefill_roofline_picks_the_binding_floor():
+    """Four new tokens per sequence on the chunked-prefill batch read 341 MB
+    of K+V for 5.4 GFLOP: HBM binds.  512 new tokens: 663 GFLOP on the same
+    bytes, the matrix cores bind.  Rates are in the bound's own unit."""
+    import bench
+    kv = 340672512
+    bound, achieved, peak, unit = bench.prefill_roofline(kv, 5449187328, "bf16", 62.5e-6)
+    assert (bound, peak, unit) == ("hbm", 8000.0, "GB/s")
+    assert abs(achieved - kv / 62.5e-6 / 1e9) < 1e-6
+    bound, achieved, peak, unit = bench.prefill_roofline(kv, 663404675072, "bf16", 950e-6)
+    assert (bound, peak, unit) == ("mfma", 2500.0, "TFLOP/s")
+    assert abs(achieved - 663404675072 / 950e-6 / 1e12) < 1e-9
+    # the crossover: equal floors stay on the matrix cores
+    assert bench.prefill_roofline(8e12, 2.5e15, "f16", 1.0)[0] == "mfma"   # one second each
+    assert bench.prefill_roofline(8.1e12, 2.5e15, "f16", 1.0)[0] == "hbm"
