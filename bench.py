@@ -576,28 +576,44 @@ def bench_prefill(args, dev):
     }
     if not args.no_cpu_baseline:
         import oracle
-        rows = list(range(w.Hq))                   # the first query row, all heads
-        oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                       pw.query_start, w.scale, rows=rows)
-        qs = pw.query_start.cpu().numpy()
-        # sample: the first rows of sequence 0 until ~cpu_seconds of work
-        n0 = int(qs[1])
+        # the inputs on the host once, so the timing is the oracle's arithmetic
+        host = [t.cpu() for t in (pw.query, w.key_cache, w.value_cache, w.block_tables,
+                                  w.seq_lens, pw.query_start)]
+        import numpy as np
+        qs = host[5].numpy().astype(np.int64)
+        lens = host[4].numpy().astype(np.int64)
+        # tokens each query row attends (row k of sequence s sits at L_s - n_s + k)
+        att = np.concatenate([np.arange(L - n + 1, L + 1) for L, n in zip(lens, np.diff(qs))])
+        # size the sample on the first few rows (after one untimed call)
+        probe = min(8, len(att))
+        rows = list(range(probe * w.Hq))
+        oracle.prefill(*host, w.scale, rows=rows)
         t0 = time.perf_counter()
-        oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                       pw.query_start, w.scale, rows=rows)
-        t_one = max(time.perf_counter() - t0, 1e-6)
-        nrows = max(1, min(n0, int(args.cpu_seconds / t_one)))
+        oracle.prefill(*host, w.scale, rows=rows)
+        per_tok = max(time.perf_counter() - t0, 1e-6) / max(int(att[:probe].sum()), 1)
+        cum = np.cumsum(att)
+
+        def rows_for(seconds):
+            return max(1, min(int(np.searchsorted(cum, seconds / per_tok)) + 1, len(att)))
+
+        # a call has a fixed cost the probe overweights: re-estimate on a
+        # quarter of the target before sizing the sample
+        n1 = rows_for(args.cpu_seconds / 4)
+        t0 = time.perf_counter()
+        oracle.prefill(*host, w.scale, rows=list(range(n1 * w.Hq)))
+        per_tok = max(time.perf_counter() - t0, 1e-6) / int(cum[n1 - 1])
+        # sample: the first query rows, all heads, through as many sequences
+        # as about cpu_seconds of work take
+        nrows = rows_for(args.cpu_seconds)
         rows = list(range(nrows * w.Hq))
         t0 = time.perf_counter()
-        oracle.prefill(pw.query, w.key_cache, w.value_cache, w.block_tables, w.seq_lens,
-                       pw.query_start, w.scale, rows=rows)
+        oracle.prefill(*host, w.scale, rows=rows)
         dt = time.perf_counter() - t0
-        L0, n_0 = int(w.lens[0]), n0
-        toks = sum(L0 - n_0 + k + 1 for k in range(nrows))
+        toks = int(att[:nrows].sum())
         res["cpu_baseline"] = {"value": round(4 * w.D * w.Hq * toks / dt / 1e12, 6), "unit": "TFLOP/s",
                                "cores": oracle.num_threads(), "cpu": cpu_model(),
                                "kind": "oracle",
-                               "sample": f"first {nrows} query rows of sequence 0, all heads",
+                               "sample": f"the first {nrows} of {len(att)} query rows, all heads",
                                "seconds": round(dt, 2)}
     print(json.dumps(res), flush=True)
 
