@@ -9,7 +9,7 @@ GPU: the library against the oracle on identical inputs (both kernels, every
 group size, block sizes 1..32, forced partitions, ragged chunks, and a seeded
 sweep of random shapes over all of these), an exact
 needle check of positions, staged calls, and the benchmark-sized workload on
-sampled rows.
+every (query row, head).
 """
 import json
 import math
